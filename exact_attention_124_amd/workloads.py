@@ -1,0 +1,113 @@
+"""Seeded synthetic workloads for attention forward.
+
+This module draws inputs and picks which slices/rows to check.  It holds none
+of attention's arithmetic, so the HIP path and the fp64 oracle can both be fed
+from it without sharing any computation.
+
+Recipe (the pages name no data; these shapes follow the score-matrix sizes and
+head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
+
+* ``torch.Generator('cpu').manual_seed(seed)``, then ``Q``, ``K``, ``V`` drawn
+  in that order as float32 ``randn`` of shape ``[B, H, N, d]``;
+* ``Q`` multiplied by ``q_mult`` (8 for the long-context stress case, a power
+  of two, so exact before or after rounding);
+* converted to the working dtype with ``Tensor.to`` (round to nearest even for
+  bfloat16);
+* slices to check against the oracle: ``randperm(B*H)`` from a second
+  generator seeded with ``seed + 1``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: torch.dtype
+    causal: bool
+    q_mult: float = 1.0
+    oracle_slices: int | None = None   # None = every (b, h) slice
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """Dense-contraction FLOP convention: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def elem_bytes(self) -> int:
+        return torch.tensor([], dtype=self.dtype).element_size()
+
+    def describe(self) -> str:
+        dt = {torch.bfloat16: "bf16", torch.float32: "fp32"}[self.dtype]
+        mask = "causal" if self.causal else "non-causal"
+        extra = f", Q x{self.q_mult:g}" if self.q_mult != 1.0 else ""
+        return f"{mask} attention fwd B={self.B} H={self.H} N={self.N} d={self.d} {dt}{extra}"
+
+
+# The five workloads, smallest first.
+WORKLOADS = {
+    "small_fp32": Workload("small_fp32", 1, 1, 128, 64, torch.float32, False),
+    "gpt2_heads_bf16": Workload("gpt2_heads_bf16", 1, 12, 1024, 64, torch.bfloat16, False),
+    "causal_2k_bf16": Workload("causal_2k_bf16", 4, 32, 2048, 128, torch.bfloat16, True),
+    "dense_8k_bf16": Workload("dense_8k_bf16", 8, 32, 8192, 128, torch.bfloat16, False,
+                              oracle_slices=4),
+    "causal_32k_qx8_bf16": Workload("causal_32k_qx8_bf16", 1, 32, 32768, 128, torch.bfloat16,
+                                    True, q_mult=8.0, oracle_slices=2),
+}
+ORDER = ["small_fp32", "gpt2_heads_bf16", "causal_2k_bf16", "dense_8k_bf16",
+         "causal_32k_qx8_bf16"]
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0,
+             q_mult: float = 1.0, device="cpu"):
+    """Draw Q, K, V as described in the module docstring."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if q_mult != 1.0:
+        q.mul_(q_mult)
+    out = []
+    for t in (q, k, v):
+        t = t.to(dtype)
+        out.append(t.to(device) if str(device) != "cpu" else t)
+    return tuple(out)
+
+
+def workload_inputs(w: Workload, device="cpu"):
+    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.q_mult, device)
+
+
+def check_slices(w: Workload) -> list[int]:
+    """Flattened (b*H + h) slice indices the oracle checks for workload ``w``."""
+    n = w.B * w.H
+    if w.oracle_slices is None or w.oracle_slices >= n:
+        return list(range(n))
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+    return torch.randperm(n, generator=g)[: w.oracle_slices].tolist()
+
+
+def sample_rows(N: int, count: int, seed: int = 2) -> list[int]:
+    """``count`` distinct seeded query rows in [0, N), always including the
+    first and the last row (the causal extremes), sorted."""
+    if count >= N:
+        return list(range(N))
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    picks = set(torch.randperm(N, generator=g)[: max(count - 2, 0)].tolist())
+    picks.update({0, N - 1})
+    return sorted(picks)

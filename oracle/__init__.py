@@ -1,0 +1,108 @@
+"""fp64 CPU oracle for scaled dot-product attention.
+
+Test infrastructure, not product code: only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+it.  The HIP library neither imports nor links anything here, and this package
+imports nothing from the HIP library.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, the textbook
+definition: scores, row max, exp-sum, weighted values).  This module only
+builds that file with gcc and marshals numpy arrays through ctypes.
+
+Definition followed: grasp.study lesson on standard self-attention, section
+"The Computational Steps of Standard Self-Attention" (scores = Q K^T, row-wise
+softmax, output = P V), with the exactness claim of "Attention Is
+Memory-Bound, and Nobody Noticed for Five Years" (the fused method returns the
+same function up to floating-point reassociation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``attn_oracle.c`` into ``liboracle.so`` with gcc (fp64, no FMA
+    contraction, OpenMP over rows).  Returns the library path."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_attn_f64.restype = ctypes.c_int
+    lib.oracle_attn_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,   # q k v
+        ctypes.c_void_p, ctypes.c_void_p,                    # o lse
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,      # S N d
+        ctypes.c_double, ctypes.c_int,                       # scale causal
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,       # rows n_rows threads
+    ]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle uses by default."""
+    return int(_load().oracle_max_threads())
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: exact upcast on the CPU
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def attention(q, k, v, scale: float, causal: bool = False, rows=None, threads: int = 0):
+    """Exact attention in fp64.
+
+    ``q``, ``k``, ``v``: arrays of shape ``[..., N, d]`` (any leading dims are
+    flattened into independent slices).  ``rows``: optional 1-D sequence of
+    query-row indices to compute (every slice); ``None`` = all rows.
+    Returns ``(o, lse)`` with shapes ``[..., R, d]`` and ``[..., R]``.
+    """
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    if not (q64.shape == k64.shape == v64.shape) or q64.ndim < 2:
+        raise ValueError("q, k, v must share one shape [..., N, d]")
+    lead = q64.shape[:-2]
+    N, d = q64.shape[-2:]
+    S = int(np.prod(lead)) if lead else 1
+    if rows is None:
+        R = N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        R = rows_arr.size
+    o = np.empty((S, R, d), dtype=np.float64)
+    lse = np.empty((S, R), dtype=np.float64)
+    rc = _load().oracle_attn_f64(
+        q64.ctypes.data, k64.ctypes.data, v64.ctypes.data,
+        o.ctypes.data, lse.ctypes.data,
+        S, N, d, float(scale), 1 if causal else 0,
+        rows_arr.ctypes.data if rows_arr is not None else None,
+        R if rows_arr is not None else 0, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_f64 failed with code {rc}")
+    return o.reshape(*lead, R, d), lse.reshape(*lead, R)
