@@ -1,0 +1,222 @@
+"""Exact fused attention forward for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/attn.h`` (``libattn.so``):
+argument marshalling only.  Every step of the computation runs in the HIP
+kernels of that library; PyTorch supplies device memory and the stream.  If
+the library has not been built, every call raises -- there is no fallback.
+
+Functions with the C names take caller-allocated tensors, exactly like the C
+entry points; ``attention`` and ``attention_unfused`` allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "library_path", "load_library", "attn_fwd", "attn_fwd_f32", "attn_fwd_unfused",
+    "attn_fwd_unfused_f32", "attn_unfused_workspace_bytes", "attn_status_string",
+    "attn_last_hip_error", "attention", "attention_unfused", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+# attn_status values (include/attn.h)
+STATUS = {
+    "ATTN_OK": 0, "ATTN_ERR_NULL": 1, "ATTN_ERR_SHAPE": 2, "ATTN_ERR_HEAD_DIM": 3,
+    "ATTN_ERR_ALIGN": 4, "ATTN_ERR_ALIAS": 5, "ATTN_ERR_WORKSPACE": 6, "ATTN_ERR_HIP": 7,
+    "ATTN_ERR_ARG": 8,
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {attn_status_string(status)} (status {status})"
+        if status == STATUS["ATTN_ERR_HIP"]:
+            msg += f", hipError_t {attn_last_hip_error()}"
+        super().__init__(msg)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``libattn.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m exact_attention_124_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd = [P, P, P, P, P, I, I, I, I, F, I, P]
+    unf = [P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
+    for name, args in (("attn_fwd", fwd), ("attn_fwd_f32", fwd),
+                       ("attn_fwd_unfused", unf), ("attn_fwd_unfused_f32", unf)):
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I
+    lib.attn_unfused_workspace_bytes.argtypes = [I, I, I, I]
+    lib.attn_unfused_workspace_bytes.restype = SZ
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = I
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_last_hip_error() -> int:
+    return int(load_library().attn_last_hip_error())
+
+
+def attn_unfused_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
+    return int(load_library().attn_unfused_workspace_bytes(B, H, N, elem_bytes))
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers (torch is only a container for device memory here).
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _check_qkv(q, k, v, dtype):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must live on a GPU")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    return tuple(q.shape)
+
+
+def _check_out(o, lse, shape, dtype, device):
+    torch = _torch()
+    if o.dtype != dtype or tuple(o.shape) != shape or not o.is_contiguous() or o.device != device:
+        raise ValueError("o must be a contiguous tensor like q")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != shape[:3] or not lse.is_contiguous() \
+                or lse.device != device:
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _fwd(name, dtype, q, k, v, o, lse, causal, scale, stream):
+    B, H, N, d = _check_qkv(q, k, v, dtype)
+    _check_out(o, lse, (B, H, N, d), dtype, q.device)
+    fn = getattr(load_library(), name)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+            B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, name)
+
+
+def _unfused(name, dtype, elem, q, k, v, o, lse, workspace, causal, scale, stream):
+    B, H, N, d = _check_qkv(q, k, v, dtype)
+    _check_out(o, lse, (B, H, N, d), dtype, q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    fn = getattr(load_library(), name)
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+            workspace.data_ptr(), nbytes, B, H, N, d, _scale(scale, d), 1 if causal else 0,
+            _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, name)
+
+
+# ---------------------------------------------------------------------------
+# Same names as the C entry points.
+# ---------------------------------------------------------------------------
+def attn_fwd(q, k, v, o, lse=None, causal=False, scale=None, stream=None):
+    """bf16 fused forward into caller-allocated ``o`` (and ``lse``)."""
+    _fwd("attn_fwd", _torch().bfloat16, q, k, v, o, lse, causal, scale, stream)
+
+
+def attn_fwd_f32(q, k, v, o, lse=None, causal=False, scale=None, stream=None):
+    """fp32 fused forward into caller-allocated ``o`` (and ``lse``)."""
+    _fwd("attn_fwd_f32", _torch().float32, q, k, v, o, lse, causal, scale, stream)
+
+
+def attn_fwd_unfused(q, k, v, o, lse, workspace, causal=False, scale=None, stream=None):
+    """bf16 unfused forward (scores and probabilities in ``workspace``)."""
+    _unfused("attn_fwd_unfused", _torch().bfloat16, 2, q, k, v, o, lse, workspace, causal, scale,
+             stream)
+
+
+def attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal=False, scale=None, stream=None):
+    """fp32 unfused forward (scores and probabilities in ``workspace``)."""
+    _unfused("attn_fwd_unfused_f32", _torch().float32, 4, q, k, v, o, lse, workspace, causal,
+             scale, stream)
+
+
+# ---------------------------------------------------------------------------
+# Allocating conveniences.
+# ---------------------------------------------------------------------------
+def attention(q, k, v, causal=False, scale=None, stream=None):
+    """Fused forward; returns ``(o, lse)``.  bf16 or fp32 by ``q.dtype``."""
+    torch = _torch()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        attn_fwd(q, k, v, o, lse, causal, scale, stream)
+    elif q.dtype == torch.float32:
+        attn_fwd_f32(q, k, v, o, lse, causal, scale, stream)
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return o, lse
+
+
+def attention_unfused(q, k, v, causal=False, scale=None, stream=None, workspace=None):
+    """Unfused forward; returns ``(o, lse, workspace)`` (workspace holds P)."""
+    torch = _torch()
+    B, H, N, _ = q.shape
+    elem = 2 if q.dtype == torch.bfloat16 else 4
+    if workspace is None:
+        workspace = torch.empty(attn_unfused_workspace_bytes(B, H, N, elem), dtype=torch.uint8,
+                                device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        attn_fwd_unfused(q, k, v, o, lse, workspace, causal, scale, stream)
+    elif q.dtype == torch.float32:
+        attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal, scale, stream)
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return o, lse, workspace

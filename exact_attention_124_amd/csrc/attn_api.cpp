@@ -1,0 +1,170 @@
+// C-ABI entry points: argument validation, then one dispatch to the kernel
+// launchers.  Nothing here touches the device before validation has passed.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shared checks of every forward entry point.  Returns ATTN_OK to proceed,
+// a negative value for "valid but empty" (nothing to do), or an error code.
+int validate_common(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                    int B, int H, int N, int d, float scale, int causal, size_t elem) {
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return -1;  // empty: no memory is touched, NULL allowed
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_ERR_ARG;
+    if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_ERR_ALIGN;
+    if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+    // Per-slice byte offsets are 32-bit inside the kernels (buffer resources),
+    // including one padded block of rows past the end.
+    const uint64_t slice_bytes = (uint64_t)(N + 2 * attn::kFwdBlockRows) * (uint64_t)d * elem;
+    if (slice_bytes >= (1ull << 32)) return ATTN_ERR_SHAPE;
+    const uint64_t BH = (uint64_t)B * (uint64_t)H;
+    if (BH >= (1ull << 31)) return ATTN_ERR_SHAPE;
+    const uint64_t blocks = BH * (uint64_t)((N + attn::kFwdBlockRows - 1) / attn::kFwdBlockRows);
+    if (blocks >= (1ull << 31)) return ATTN_ERR_SHAPE;
+    const size_t tensor = (size_t)BH * (size_t)N * (size_t)d * elem;
+    const Range rq = range_of(q, tensor), rk = range_of(k, tensor), rv = range_of(v, tensor);
+    const Range ro = range_of(o, tensor);
+    if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv)) return ATTN_ERR_ALIAS;
+    if (lse) {
+        const Range rl = range_of(lse, (size_t)BH * (size_t)N * sizeof(float));
+        if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) || overlaps(rl, ro)) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+int finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
+attn::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                        int N, int d, float scale, int causal) {
+    attn::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.N = N;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    return a;
+}
+
+int validate_workspace(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                       const void *ws, size_t ws_bytes, int B, int H, int N, int d, size_t elem) {
+    if (!ws) return ATTN_ERR_NULL;
+    const size_t need = attn_unfused_workspace_bytes(B, H, N, (int)elem);
+    if (need == 0 || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+    const size_t tensor = (size_t)B * H * (size_t)N * d * elem;
+    const Range rw = range_of(ws, need);
+    if (overlaps(rw, range_of(q, tensor)) || overlaps(rw, range_of(k, tensor)) ||
+        overlaps(rw, range_of(v, tensor)) || overlaps(rw, range_of(o, tensor)))
+        return ATTN_ERR_ALIAS;
+    if (lse && overlaps(rw, range_of(lse, (size_t)B * H * (size_t)N * sizeof(float)))) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+             float scale, int causal, hipStream_t stream) {
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    return finish(attn::launch_fwd_bf16(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), stream));
+}
+
+int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H, int N,
+                 int d, float scale, int causal, hipStream_t stream) {
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    return finish(attn::launch_fwd_f32(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), stream));
+}
+
+size_t attn_unfused_workspace_bytes(int B, int H, int N, int elem_bytes) {
+    if (B <= 0 || H <= 0 || N <= 0 || elem_bytes <= 0) return 0;
+    const unsigned __int128 n = (unsigned __int128)B * (unsigned)H * (unsigned)N * (unsigned)N *
+                                (unsigned)elem_bytes;
+    if (n > (unsigned __int128)SIZE_MAX) return 0;
+    return (size_t)n;
+}
+
+int attn_fwd_unfused(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                     hipStream_t stream) {
+    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    st = validate_workspace(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, 2);
+    if (st != ATTN_OK) return st;
+    // Score-kernel grid: B*H * ceil(N/128)^2 workgroups.
+    const uint64_t nb = (uint64_t)((N + 127) / 128);
+    if ((uint64_t)B * H * nb * nb >= (1ull << 31)) return ATTN_ERR_SHAPE;
+    return finish(attn::launch_unfused_bf16(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), workspace,
+                                            stream));
+}
+
+int attn_fwd_unfused_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                         void *workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                         int causal, hipStream_t stream) {
+    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    st = validate_workspace(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, 4);
+    if (st != ATTN_OK) return st;
+    const uint64_t nb = (uint64_t)((N + 63) / 64);
+    if ((uint64_t)B * H * nb * nb >= (1ull << 31)) return ATTN_ERR_SHAPE;
+    return finish(attn::launch_unfused_f32(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), workspace,
+                                           stream));
+}
+
+const char *attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid or too large B, H or N";
+        case ATTN_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+        case ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse 4 bytes)";
+        case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+        case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_unfused_workspace_bytes()";
+        case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
+        case ATTN_ERR_ARG: return "scale must be finite and > 0, causal must be 0 or 1";
+        default: return "unknown status";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

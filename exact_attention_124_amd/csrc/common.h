@@ -1,0 +1,90 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Raw buffer resource over `bytes` bytes at `base`.  Loads past the end return
+// zero and stores past the end are dropped, which handles ragged tails without
+// branches.  `bytes` must be below 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4 x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(u32x2 x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: C(32x32) += A(32x16) * B(16x32).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 8 values
+// along the contraction; the two lane halves (l / 32) carry the two halves of
+// the 16-long contraction.  Result: lane l holds column (l % 32) and rows
+// 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_permlane32_swap exchanges the two 32-lane halves of a wave; with the same
+// register as both operands, every lane ends up holding {x[l], x[l ^ 32]} in
+// its two results.  Max and sum over that pair are symmetric, so they do not
+// depend on which result carries which half.
+__device__ __forceinline__ float pair_max(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> two bf16 (round to nearest even) packed low/high in one word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Block index remap so that consecutive logical blocks land on the same XCD.
+// The dispatcher hands workgroup i to XCD (i % 8); this inverts that so the
+// blocks of one attention head share one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    const int xcd = bid & 7;
+    const int local = bid >> 3;
+    const int per = nblocks >> 3;
+    const int rem = nblocks & 7;
+    const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+    return start + local;
+}
+
+}  // namespace attn

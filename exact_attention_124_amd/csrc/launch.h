@@ -1,0 +1,37 @@
+// Internal launch interface between the C-ABI entry points (attn_api.cpp)
+// and the kernel translation units.  Every launcher assumes its arguments have
+// already been validated by the entry point and returns the hipError_t of the
+// launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;  // may be null
+    int BH;      // B * H slices
+    int N;
+    int d;
+    float scale;
+    int causal;
+};
+
+// Fused forward (one kernel launch).
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
+
+// Unfused forward: scores -> workspace, softmax in place, probabilities x V.
+hipError_t launch_unfused_bf16(const FwdArgs &a, void *ws, hipStream_t s);
+hipError_t launch_unfused_f32(const FwdArgs &a, void *ws, hipStream_t s);
+
+// Query-row block of the fused bf16 kernel (used for grid-size limits).
+constexpr int kFwdBlockRows = 128;
+
+}  // namespace attn

@@ -1,0 +1,121 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact attention forward library.
+ *
+ * The operation (grasp.study lesson on standard self-attention, section "The
+ * Computational Steps of Standard Self-Attention"; "Attention Is Memory-Bound,
+ * and Nobody Noticed for Five Years", exactness paragraphs):
+ *
+ *     o[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,h,j,:] ) * v[b,h,j,:]
+ *     lse[b,h,i] = ln sum_j exp( scale * q[b,h,i,:] . k[b,h,j,:] )
+ *
+ * where j runs over every key (causal = 0) or over j <= i (causal = 1).
+ * attn_fwd / attn_fwd_f32 compute it fused, in one kernel per block of query
+ * rows: scores, the running (max, sum) softmax and the value weighting stay
+ * on chip and only o and lse reach memory ("The Attention Bottleneck -- and How
+ * FlashAttention Fixed It", section "The fix: tiling and fusion, never touch
+ * HBM").  attn_fwd_unfused / attn_fwd_unfused_f32 compute the same function the
+ * standard way, as separate launches that write the N x N score matrix and the
+ * probability matrix to device memory and read them back (the trace of a
+ * textbook implementation on "Attention Is Memory-Bound ..."): they exist to
+ * measure that memory-bound path on the same chip.
+ *
+ * Layout.  q, k, v and o are dense row-major [B, H, N, d] tensors (d fastest,
+ * then N, then H, then B) with no padding between rows; lse is a dense
+ * [B, H, N] float array.  The unfused workspace holds one [B, H, N, N] matrix.
+ *
+ * Ownership.  Every pointer is a device pointer owned by the caller, who
+ * allocates and frees it.  The library allocates, frees and synchronises
+ * nothing; it only enqueues kernels on `stream` (0 = the null stream) and
+ * returns.  Errors raised while the kernels run surface at the caller's next
+ * synchronisation of that stream.
+ *
+ * Errors.  Arguments are validated, in the order listed on each function,
+ * before any HIP call.  A failing check returns its status code and enqueues
+ * nothing; there is never a silent fallback to another algorithm.  A HIP
+ * launch failure returns ATTN_ERR_HIP; attn_last_hip_error() then gives the
+ * hipError_t for the calling thread.  No C++ exception crosses this ABI.  All
+ * calls are thread-safe (the only mutable state is the thread-local error).
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* a required pointer is NULL                                 */
+    ATTN_ERR_SHAPE = 2,     /* B, H or N negative, or a size limit below exceeded          */
+    ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                         */
+    ATTN_ERR_ALIGN = 4,     /* q, k, v, o or workspace not 16-byte aligned; lse not 4-byte */
+    ATTN_ERR_ALIAS = 5,     /* an output range overlaps an input or another output range   */
+    ATTN_ERR_WORKSPACE = 6, /* unfused workspace smaller than attn_unfused_workspace_bytes */
+    ATTN_ERR_HIP = 7,       /* a HIP runtime call failed (see attn_last_hip_error)        */
+    ATTN_ERR_ARG = 8        /* scale not finite and > 0, or causal not 0/1                */
+} attn_status;
+
+/*
+ * Fused forward, bfloat16.
+ *   q, k, v : const bf16 [B,H,N,d] inputs (raw 16-bit bfloat16 words)
+ *   o       : bf16 [B,H,N,d] output, rounded to nearest even from fp32
+ *   lse     : float [B,H,N] natural-log log-sum-exp of the scaled, masked
+ *             scores, or NULL to skip it
+ *   scale   : multiplies q.k (usually 1/sqrt(d)); must be finite and > 0
+ *   causal  : 0 = every key, 1 = key j allowed for query i iff j <= i
+ * Products accumulate in fp32 on the matrix cores; the softmax runs in fp32
+ * with base-2 exponentials; the probabilities feed the second product as bf16.
+ * Checks, in order: B,H,N >= 0 (any zero: return ATTN_OK, nothing enqueued,
+ * pointers may then be NULL) -> NULL (q,k,v,o) -> d in {64,128} -> scale,
+ * causal -> alignment -> limits ((N+256)*d*elem_bytes < 2^32 per slice,
+ * B*H < 2^31, workgroups < 2^31) -> o and lse do not overlap q, k, v or each
+ * other.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Fused forward, float32 in and out, fp32 arithmetic throughout (vector
+ * units, no reduced-precision step).  Same parameters and checks as attn_fwd. */
+int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                 int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Bytes of workspace the unfused variant needs: B*H*N*N*elem_bytes
+ * (elem_bytes = 2 for attn_fwd_unfused, 4 for attn_fwd_unfused_f32).  Returns
+ * 0 for non-positive arguments or on size_t overflow.  Pure host function. */
+size_t attn_unfused_workspace_bytes(int B, int H, int N, int elem_bytes);
+
+/*
+ * Unfused forward, bfloat16: three launches on `stream`.
+ *   1. scores: workspace <- q k^T (raw dot products, rounded to bf16)
+ *   2. softmax: per row, scale, mask, subtract the max, exponentiate,
+ *      normalise; the bf16 probabilities overwrite the scores in place; lse
+ *   3. output: o <- P v
+ * workspace: device buffer of at least attn_unfused_workspace_bytes(B,H,N,2)
+ * bytes, 16-byte aligned, not overlapping q, k, v, o or lse; its contents on
+ * return are the probabilities P [B,H,N,N].
+ * Checks: as attn_fwd, then workspace NULL (ATTN_ERR_NULL), size
+ * (ATTN_ERR_WORKSPACE), alignment and overlap.
+ */
+int attn_fwd_unfused(const void *q, const void *k, const void *v, void *o, float *lse,
+                     void *workspace, size_t workspace_bytes,
+                     int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Unfused forward, float32 scores and probabilities (workspace elem_bytes 4). */
+int attn_fwd_unfused_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                         void *workspace, size_t workspace_bytes,
+                         int B, int H, int N, int d, float scale, int causal,
+                         hipStream_t stream);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char *attn_status_string(int status);
+
+/* hipError_t of the calling thread's last ATTN_ERR_HIP (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EXACT_ATTENTION_ATTN_H */

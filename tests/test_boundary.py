@@ -1,0 +1,158 @@
+"""C-ABI boundary on the CPU: the library loads, exports what include/attn.h
+declares, sizes the unfused workspace as the pages count the score matrix,
+and rejects bad arguments with status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_attention_124_amd as ea
+    if not os.path.exists(ea.library_path()):
+        from exact_attention_124_amd import build
+        build.build()
+    return ea.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_unfused", "attn_fwd_unfused_f32",
+                            "attn_unfused_workspace_bytes", "attn_status_string",
+                            "attn_last_hip_error"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_status_strings(lib):
+    import exact_attention_124_amd as ea
+    for code in range(9):
+        s = ea.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert ea.attn_status_string(99) == "unknown status"
+    assert ea.attn_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("N,expected", [(2048, 8_388_608), (4096, 33_554_432),
+                                        (8192, 134_217_728), (16384, 536_870_912)])
+def test_workspace_reproduces_per_head_score_sizes(lib, N, expected):
+    # "Attention Is Memory-Bound, and Nobody Noticed for Five Years", score-matrix
+    # size paragraph: one 16-bit head is 8.4 / 33.6 / 134.2 / 536.9 MB at
+    # 2,048 / 4,096 / 8,192 / 16,384 tokens.
+    import exact_attention_124_amd as ea
+    got = ea.attn_unfused_workspace_bytes(1, 1, N, 2)
+    assert got == expected
+    assert round(got / 1e6, 1) == {2048: 8.4, 4096: 33.6, 8192: 134.2, 16384: 536.9}[N]
+
+
+def test_workspace_reproduces_batch_figure_and_traffic(lib):
+    # Same page: batch 8 x 32 heads x 8,192 tokens needs 34.4 GB of scores; four
+    # crossings are ~138 GB, ~70 ms at ~2 TB/s.
+    import exact_attention_124_amd as ea
+    s = ea.attn_unfused_workspace_bytes(8, 32, 8192, 2)
+    assert s == 34_359_738_368
+    assert round(s / 1e9, 1) == 34.4
+    assert round(4 * s / 1e9) == 137  # the page rounds 4 x 34.4 up to 138
+    assert 65 <= 4 * s / 2e12 * 1e3 <= 70
+
+
+def test_workspace_edge_cases(lib):
+    import exact_attention_124_amd as ea
+    assert ea.attn_unfused_workspace_bytes(0, 1, 1, 2) == 0
+    assert ea.attn_unfused_workspace_bytes(1, 1, -5, 2) == 0
+    assert ea.attn_unfused_workspace_bytes(2**31 - 1, 2**31 - 1, 2**31 - 1, 4) == 0  # overflow
+    assert ea.attn_unfused_workspace_bytes(3, 5, 7, 4) == 3 * 5 * 7 * 7 * 4
+
+
+# Fake, well-separated, aligned device addresses: validation never dereferences them.
+A = 1 << 40
+GAP = 1 << 36
+Q, K, V, O, L, W = (A + i * GAP for i in range(6))
+
+
+def fwd(lib, name="attn_fwd", q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=256, d=64, scale=0.125,
+        causal=0):
+    return getattr(lib, name)(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+def unf(lib, name="attn_fwd_unfused", ws=W, ws_bytes=None, B=1, H=2, N=256, d=64, elem=2, **kw):
+    if ws_bytes is None:
+        ws_bytes = B * H * N * N * elem
+    args = dict(q=Q, k=K, v=V, o=O, lse=L)
+    args.update(kw)
+    return getattr(lib, name)(args["q"], args["k"], args["v"], args["o"], args["lse"], ws, ws_bytes,
+                              B, H, N, d, 0.125, 0, None)
+
+
+@pytest.mark.parametrize("name", ["attn_fwd", "attn_fwd_f32"])
+def test_validation_codes(lib, name):
+    S = {k: v for k, v in __import__("exact_attention_124_amd").STATUS.items()}
+    assert fwd(lib, name, q=None) == S["ATTN_ERR_NULL"]
+    assert fwd(lib, name, o=None) == S["ATTN_ERR_NULL"]
+    assert fwd(lib, name, N=-1) == S["ATTN_ERR_SHAPE"]
+    assert fwd(lib, name, B=-2) == S["ATTN_ERR_SHAPE"]
+    assert fwd(lib, name, N=0) == S["ATTN_OK"]          # empty: nothing enqueued
+    assert fwd(lib, name, H=0, d=3) == S["ATTN_OK"]     # empty wins over other checks
+    assert fwd(lib, name, N=0, q=None, k=None, v=None, o=None, lse=None) == S["ATTN_OK"]
+    for d in (0, 32, 96, 100, 256):
+        assert fwd(lib, name, d=d) == S["ATTN_ERR_HEAD_DIM"]
+    assert fwd(lib, name, scale=0.0) == S["ATTN_ERR_ARG"]
+    assert fwd(lib, name, scale=-1.0) == S["ATTN_ERR_ARG"]
+    assert fwd(lib, name, scale=float("nan")) == S["ATTN_ERR_ARG"]
+    assert fwd(lib, name, scale=float("inf")) == S["ATTN_ERR_ARG"]
+    assert fwd(lib, name, causal=2) == S["ATTN_ERR_ARG"]
+    assert fwd(lib, name, q=Q + 8) == S["ATTN_ERR_ALIGN"]
+    assert fwd(lib, name, o=O + 4) == S["ATTN_ERR_ALIGN"]
+    assert fwd(lib, name, lse=L + 2) == S["ATTN_ERR_ALIGN"]
+    assert fwd(lib, name, o=Q) == S["ATTN_ERR_ALIAS"]
+    assert fwd(lib, name, o=V + 4096) == S["ATTN_ERR_ALIAS"]
+    assert fwd(lib, name, lse=K + 16) == S["ATTN_ERR_ALIAS"]
+    assert fwd(lib, name, lse=O + 256) == S["ATTN_ERR_ALIAS"]
+    assert fwd(lib, name, N=1 << 26, d=128) == S["ATTN_ERR_SHAPE"]  # 32-bit slice offsets
+    assert fwd(lib, name, B=1 << 16, H=1 << 16) == S["ATTN_ERR_SHAPE"]
+
+
+@pytest.mark.parametrize("name,elem", [("attn_fwd_unfused", 2), ("attn_fwd_unfused_f32", 4)])
+def test_unfused_validation_codes(lib, name, elem):
+    S = __import__("exact_attention_124_amd").STATUS
+    assert unf(lib, name, elem=elem, ws=None) == S["ATTN_ERR_NULL"]
+    assert unf(lib, name, elem=elem, ws_bytes=2 * 256 * 256 * elem - 1) == S["ATTN_ERR_WORKSPACE"]
+    assert unf(lib, name, elem=elem, ws=W + 8) == S["ATTN_ERR_ALIGN"]
+    assert unf(lib, name, elem=elem, ws=O) == S["ATTN_ERR_ALIAS"]
+    assert unf(lib, name, elem=elem, ws=L - 64) == S["ATTN_ERR_ALIAS"]
+    assert unf(lib, name, elem=elem, q=None) == S["ATTN_ERR_NULL"]
+    assert unf(lib, name, elem=elem, N=0) == S["ATTN_OK"]
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    import exact_attention_124_amd as ea
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attention(x, x, x)
+
+
+def test_no_oracle_in_product_path():
+    # The product package neither imports nor links the oracle.
+    pkg = os.path.join(ROOT, "exact_attention_124_amd")
+    pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle)|liboracle|attn_oracle", re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f"{f} refers to the oracle"

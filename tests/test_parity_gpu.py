@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (bf16 inputs, unit-variance data): over every checked element,
+max|dO| <= 2e-2 and mean|dO| <= 2e-3.  fp32 path: max|dO| <= 1e-5 * max|O_ref|
+(normwise; an element-wise relative bound is ill-posed where O ~ 0).  lse:
+fused bf16 |dlse| <= 1e-3 (it is computed from fp32 scores); fp32
+|dlse| <= 1e-5 * max(1, |lse|); unfused bf16 scores are rounded to bf16 before
+the softmax, so its lse may move by up to 2^-8 of the largest |scaled score|
+(bounded by scale * max|q| * max|k|).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 1e-3
+F32_REL = 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_124_amd as ea
+    ea.load_library()
+    return ea
+
+
+@pytest.fixture(scope="module")
+def W():
+    from exact_attention_124_amd import workloads
+    return workloads
+
+
+def check_bf16(o, lse, ro, rl, what, lse_tol=BF16_LSE):
+    o = o.double().cpu().numpy() if torch.is_tensor(o) else o
+    lse = lse.double().cpu().numpy() if torch.is_tensor(lse) else lse
+    err = np.abs(o - ro)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    mx, mean = err.max(), err.mean()
+    lerr = np.abs(lse - rl).max()
+    say(f"  {what}: max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dlse|={lerr:.3e}")
+    assert mx <= BF16_MAX, f"{what}: max abs error {mx}"
+    assert mean <= BF16_MEAN, f"{what}: mean abs error {mean}"
+    assert lerr <= lse_tol, f"{what}: lse error {lerr}"
+
+
+def check_f32(o, lse, ro, rl, what):
+    o = o.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    assert np.isfinite(o).all()
+    mx = np.abs(o - ro).max()
+    ref = np.abs(ro).max()
+    lerr = (np.abs(lse - rl) / np.maximum(1.0, np.abs(rl))).max()
+    say(f"  {what}: max|dO|/max|O|={mx / ref:.3e} max rel dlse={lerr:.3e}")
+    assert mx <= F32_REL * ref, f"{what}: normwise error {mx / ref}"
+    assert lerr <= F32_REL, f"{what}: lse error {lerr}"
+
+
+def unfused_lse_tol(q, k, scale):
+    qn = q.float().norm(dim=-1).max().item()
+    kn = k.float().norm(dim=-1).max().item()
+    return 2.0 ** -8 * scale * qn * kn + BF16_LSE
+
+
+def run(ea, q, k, v, causal, scale=None, variant="fused"):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    if variant == "fused":
+        o, lse = ea.attention(qd, kd, vd, causal=causal, scale=scale)
+    else:
+        o, lse, ws = ea.attention_unfused(qd, kd, vd, causal=causal, scale=scale)
+        del ws
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.
+# ---------------------------------------------------------------------------
+def test_small_fp32_full(ea, W, oracle_mod):
+    w = W.WORKLOADS["small_fp32"]
+    say(f"[parity] {w.describe()}")
+    q, k, v = W.workload_inputs(w)
+    ro, rl = oracle_mod.attention(q, k, v, w.scale, w.causal)
+    o, lse = run(ea, q, k, v, w.causal)
+    check_f32(o, lse, ro, rl, "fused fp32")
+    o, lse = run(ea, q, k, v, w.causal, variant="unfused")
+    check_f32(o, lse, ro, rl, "unfused fp32")
+
+
+def test_gpt2_heads_bf16_full(ea, W, oracle_mod):
+    w = W.WORKLOADS["gpt2_heads_bf16"]
+    say(f"[parity] {w.describe()}")
+    q, k, v = W.workload_inputs(w)
+    ro, rl = oracle_mod.attention(q, k, v, w.scale, w.causal)
+    o, lse = run(ea, q, k, v, w.causal)
+    check_bf16(o, lse, ro, rl, "fused bf16")
+    o, lse = run(ea, q, k, v, w.causal, variant="unfused")
+    check_bf16(o, lse, ro, rl, "unfused bf16", unfused_lse_tol(q, k, w.scale))
+
+
+def _sampled(ea, W, oracle_mod, name, rows_per_slice, extra_rows, variants=("fused",)):
+    w = W.WORKLOADS[name]
+    say(f"[parity] {w.describe()} (sampled rows)")
+    q, k, v = W.workload_inputs(w)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    slices = W.check_slices(w)
+    rows = W.sample_rows(w.N, rows_per_slice, seed=2)
+    H = w.H
+    qs = q.reshape(-1, w.N, w.d)[slices]
+    ks = k.reshape(-1, w.N, w.d)[slices]
+    vs = v.reshape(-1, w.N, w.d)[slices]
+    ro, rl = oracle_mod.attention(qs, ks, vs, w.scale, w.causal, rows=rows)
+    # a few rows of every slice, too
+    all_rows = W.sample_rows(w.N, extra_rows, seed=3)
+    ro2, rl2 = oracle_mod.attention(q.reshape(-1, w.N, w.d), k.reshape(-1, w.N, w.d),
+                                    v.reshape(-1, w.N, w.d), w.scale, w.causal, rows=all_rows)
+    for variant in variants:
+        if variant == "fused":
+            o, lse = ea.attention(qd, kd, vd, causal=w.causal)
+            tol = BF16_LSE
+        else:
+            o, lse, ws = ea.attention_unfused(qd, kd, vd, causal=w.causal)
+            del ws
+            tol = unfused_lse_tol(q, k, w.scale)
+        torch.cuda.synchronize()
+        of = o.reshape(-1, w.N, w.d)
+        lf = lse.reshape(-1, w.N)
+        sl = torch.tensor(slices, device=o.device)
+        rw = torch.tensor(rows, device=o.device)
+        check_bf16(of[sl][:, rw], lf[sl][:, rw], ro, rl,
+                   f"{variant} {len(slices)} slices x {len(rows)} rows", tol)
+        arw = torch.tensor(all_rows, device=o.device)
+        check_bf16(of[:, arw], lf[:, arw], ro2, rl2,
+                   f"{variant} all {of.shape[0]} slices x {len(all_rows)} rows", tol)
+        assert torch.isfinite(o).all().item(), "non-finite output somewhere"
+        del o, lse, of, lf
+        torch.cuda.empty_cache()
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+
+
+def test_causal_2k_bf16_sampled(ea, W, oracle_mod):
+    _sampled(ea, W, oracle_mod, "causal_2k_bf16", 96, 8, variants=("fused", "unfused"))
+
+
+def test_dense_8k_bf16_sampled(ea, W, oracle_mod):
+    _sampled(ea, W, oracle_mod, "dense_8k_bf16", 256, 6, variants=("fused", "unfused"))
+
+
+def test_causal_32k_qx8_bf16_sampled(ea, W, oracle_mod):
+    # The unfused path is not parity-gated here: its bf16 scores carry absolute
+    # errors of ~0.25 at logits near 32, beyond the 2e-2 output bound.
+    _sampled(ea, W, oracle_mod, "causal_32k_qx8_bf16", 256, 4)
+
+
+# ---------------------------------------------------------------------------
+# Ragged and degenerate shapes, full outputs.
+# ---------------------------------------------------------------------------
+EDGE_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 383, 1000]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_shapes_bf16(ea, W, oracle_mod, d, causal):
+    for N in EDGE_N:
+        q, k, v = W.make_qkv(2, 1, N, d, torch.bfloat16, seed=N)
+        ro, rl = oracle_mod.attention(q, k, v, 1 / math.sqrt(d), causal)
+        say(f"[edge] bf16 N={N} d={d} causal={causal}")
+        o, lse = run(ea, q, k, v, causal)
+        check_bf16(o, lse, ro, rl, "fused")
+        o, lse = run(ea, q, k, v, causal, variant="unfused")
+        check_bf16(o, lse, ro, rl, "unfused", unfused_lse_tol(q, k, 1 / math.sqrt(d)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_shapes_f32(ea, W, oracle_mod, d, causal):
+    for N in [1, 5, 31, 32, 33, 127, 129, 300]:
+        q, k, v = W.make_qkv(1, 2, N, d, torch.float32, seed=100 + N)
+        ro, rl = oracle_mod.attention(q, k, v, 1 / math.sqrt(d), causal)
+        say(f"[edge] fp32 N={N} d={d} causal={causal}")
+        o, lse = run(ea, q, k, v, causal)
+        check_f32(o, lse, ro, rl, "fused")
+        o, lse = run(ea, q, k, v, causal, variant="unfused")
+        check_f32(o, lse, ro, rl, "unfused")
+
+
+def test_large_logits_bf16(ea, W, oracle_mod):
+    # Q x 8 at a small size: frequent running-max rescales.
+    for causal in (False, True):
+        q, k, v = W.make_qkv(1, 4, 777, 128, torch.bfloat16, seed=7, q_mult=8.0)
+        ro, rl = oracle_mod.attention(q, k, v, 1 / math.sqrt(128), causal)
+        say(f"[edge] bf16 Qx8 N=777 causal={causal}")
+        o, lse = run(ea, q, k, v, causal)
+        check_bf16(o, lse, ro, rl, "fused")
+
+
+def test_explicit_scale(ea, W, oracle_mod):
+    q, k, v = W.make_qkv(1, 2, 300, 64, torch.bfloat16, seed=9)
+    for scale in (0.05, 0.3):
+        ro, rl = oracle_mod.attention(q, k, v, scale, True)
+        o, lse = run(ea, q, k, v, True, scale=scale)
+        check_bf16(o, lse, ro, rl, f"fused scale={scale}")
+
+
+# ---------------------------------------------------------------------------
+# Coverage, invariants, determinism, streams.
+# ---------------------------------------------------------------------------
+def test_every_output_written(ea, W):
+    for dtype, fn in ((torch.bfloat16, "attn_fwd"), (torch.float32, "attn_fwd_f32")):
+        for causal in (False, True):
+            q, k, v = (t.cuda() for t in W.make_qkv(2, 3, 333, 128, dtype, seed=5))
+            o = torch.full_like(q, float("nan"))
+            lse = torch.full(q.shape[:3], float("nan"), device=q.device)
+            getattr(ea, fn)(q, k, v, o, lse, causal=causal)
+            torch.cuda.synchronize()
+            assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item(), (fn, causal)
+
+
+def test_ones_values_give_ones(ea, W):
+    q, k, _ = W.make_qkv(1, 2, 1000, 128, torch.bfloat16, seed=11)
+    v = torch.ones_like(q)
+    for causal in (False, True):
+        o, _ = run(ea, q, k, v, causal)
+        err = (o.float() - 1).abs().max().item()
+        say(f"  V=1 causal={causal}: max|O-1|={err:.3e}")
+        assert err <= 1e-2
+
+
+def test_key_permutation_invariance(ea, W):
+    q, k, v = W.make_qkv(1, 1, 512, 64, torch.bfloat16, seed=12)
+    perm = torch.randperm(512, generator=torch.Generator().manual_seed(0))
+    o1, l1 = run(ea, q, k, v, False)
+    o2, l2 = run(ea, q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False)
+    assert (o1.float() - o2.float()).abs().max().item() <= BF16_MAX
+    assert (l1 - l2).abs().max().item() <= BF16_LSE
+
+
+def test_deterministic(ea, W):
+    q, k, v = (t.cuda() for t in W.make_qkv(2, 4, 1024, 128, torch.bfloat16, seed=13))
+    a = ea.attention(q, k, v, causal=True)
+    b = ea.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_side_stream_and_no_lse(ea, W, oracle_mod):
+    q, k, v = W.make_qkv(1, 2, 256, 64, torch.bfloat16, seed=14)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    s = torch.cuda.Stream()
+    o = torch.empty_like(qd)
+    with torch.cuda.stream(s):
+        ea.attn_fwd(qd, kd, vd, o, None, causal=False, stream=s)
+    s.synchronize()
+    ro, rl = oracle_mod.attention(q, k, v, 1 / 8, False)
+    check_bf16(o.cpu(), rl, ro, rl, "side stream, lse=NULL")
+
+
+def test_empty_inputs_are_noops(ea):
+    q = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = ea.attention(q, q, q)
+    assert o.numel() == 0
+    q = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = ea.attention(q, q, q)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+def test_rejects_bad_head_dim_on_device(ea):
+    q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ea.AttnError) as ei:
+        ea.attention(q, q, q)
+    assert ei.value.status == ea.STATUS["ATTN_ERR_HEAD_DIM"]
