@@ -1,0 +1,263 @@
+"""Benchmark: fused exact attention forward on one MI355X.
+
+A step is one call of the fused forward (attn_fwd: scores, online softmax and
+value weighting in one kernel) on the dense 8k workload: B=8, H=32, N=8192,
+d=128, bf16, non-causal, Q/K/V iid N(0,1) (seed 0).  Inputs are resident in
+device memory before timing starts.  FLOP convention: 4*B*H*N^2*d (halved
+when causal).
+
+Prints ONE JSON line.  Besides the headline value it carries:
+  roofline      -- the fused kernel against the bf16 dense MFMA peak, its
+                   average launch time from HIP events on the launch stream,
+                   and HBM traffic from rocprofv3 counters when the committed
+                   counter record matches the current kernel source;
+  cpu_baseline  -- the fp64 CPU oracle timed on a bounded sample of the same
+                   workload (the host cores of this machine);
+  sweep         -- the same fused forward on the other workloads;
+  unfused       -- the three-launch standard path on the same workload, with
+                   its algorithmic HBM bytes per second.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused attention fwd TFLOP/s (bf16) + % of MFMA peak, B·H·N²·d sweep"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_attention_124_amd/csrc/attn_fwd_bf16.hip",
+                  "exact_attention_124_amd/csrc/common.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_bf16_dense_8k_traffic.json")
+HEADLINE = "dense_8k_bf16"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_record():
+    """HBM bytes per launch from the committed rocprofv3 counter record, or None
+    if there is none or the kernel changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel changed since counters were taken"
+    return float(rec["bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Warm up, then time exactly `steps` calls; returns (total_ms, per-launch ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    total_ms = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in evs]
+    return total_ms, per
+
+
+def bench_fused(ea, w, steps, warmup):
+    import torch
+    from exact_attention_124_amd.workloads import workload_inputs
+    q, k, v = workload_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    fn_name = "attn_fwd" if w.dtype == torch.bfloat16 else "attn_fwd_f32"
+    fn = getattr(ea, fn_name)
+    call = lambda: fn(q, k, v, o, lse, causal=w.causal, stream=stream)  # noqa: E731
+    total_ms, per = time_launches(call, steps, warmup, stream)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return total_ms, per
+
+
+def bench_unfused(ea, w, steps, warmup):
+    import torch
+    from exact_attention_124_amd.workloads import workload_inputs
+    q, k, v = workload_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws = torch.empty(ea.attn_unfused_workspace_bytes(w.B, w.H, w.N, 2), dtype=torch.uint8,
+                     device=q.device)
+    stream = torch.cuda.current_stream()
+    call = lambda: ea.attn_fwd_unfused(q, k, v, o, lse, ws, causal=w.causal, stream=stream)  # noqa
+    total_ms, per = time_launches(call, steps, warmup, stream)
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return total_ms, per
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size (for scaling the byte counters)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def cpu_baseline(w, target_s=15.0):
+    """Time the fp64 oracle on a bounded sample of workload `w` -- every query row
+    of a seeded subset of (b, h) slices, sized for about `target_s` seconds --
+    and scale to TFLOP/s with the same FLOP convention."""
+    import torch
+    import oracle
+    from exact_attention_124_amd.workloads import make_qkv
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.q_mult)
+    order = torch.randperm(w.B * w.H, generator=torch.Generator().manual_seed(w.seed + 1)).tolist()
+    q = q.reshape(-1, w.N, w.d)
+    k = k.reshape(-1, w.N, w.d)
+    v = v.reshape(-1, w.N, w.d)
+    threads = oracle.max_threads()
+    # calibration: a strided eighth of one slice's rows
+    rows = list(range(0, w.N, 8))
+    s0 = order[:1]
+    t0 = time.perf_counter()
+    oracle.attention(q[s0], k[s0], v[s0], w.scale, w.causal, rows=rows, threads=threads)
+    per_slice = (time.perf_counter() - t0) * 8
+    n_sl = int(max(1, min(len(order), round(target_s / max(per_slice, 1e-6)))))
+    sl = order[:n_sl]
+    t0 = time.perf_counter()
+    oracle.attention(q[sl], k[sl], v[sl], w.scale, w.causal, threads=threads)
+    secs = time.perf_counter() - t0
+    keys = (w.N * (w.N + 1) // 2) if w.causal else w.N * w.N
+    flops = 4.0 * w.d * keys * n_sl
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{w.name}: all {w.N} query rows of {n_sl} seeded (b,h) slices of {w.B * w.H}, "
+                       f"fp64, {secs:.1f} s"),
+            "seconds": round(secs, 3), "flop": flops}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline only: no sweep, unfused or CPU leg")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the kernel on one GPU's share of the work); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_124_amd as ea
+    from exact_attention_124_amd.workloads import ORDER, WORKLOADS
+
+    ea.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    w = WORKLOADS[HEADLINE]
+    log(f"[bench] headline: {w.describe()}, warmup {args.warmup}, steps {args.steps}")
+    total_ms, per = bench_fused(ea, w, args.steps, args.warmup)
+    ms_step = total_ms / args.steps
+    launch_ms = sum(per) / len(per)
+    value = w.flops / (ms_step * 1e-3) / 1e12
+    achieved = w.flops / (launch_ms * 1e-3) / 1e12
+    traffic, traffic_src = traffic_from_record()
+    log(f"[bench] {ms_step:.3f} ms/step, launch {launch_ms:.3f} ms, {achieved:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q, K, V, rounded to bf16)",
+        "config": {"workload": f"{w.name}: {w.describe()}", "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "traffic_source": traffic_src,
+                     "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "avg_launch_ms": round(launch_ms, 4),
+                     "flop_per_launch": w.flops},
+    }
+
+    if args.calibrate_copy:
+        copy_calibration()
+
+    if not args.quick:
+        sweep = []
+        for name in ORDER:
+            if name == HEADLINE:
+                continue
+            ww = WORKLOADS[name]
+            tot, pl = bench_fused(ea, ww, max(5, args.steps // 2), 3)
+            lm = sum(pl) / len(pl)
+            sweep.append({"workload": name, "desc": ww.describe(), "launch_ms": round(lm, 4),
+                          "TFLOP/s": round(ww.flops / (lm * 1e-3) / 1e12, 2),
+                          "frac_bf16_peak": round(ww.flops / (lm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+            log(f"[bench] sweep {name}: {lm:.4f} ms, {sweep[-1]['TFLOP/s']} TFLOP/s")
+        sweep.insert(3, {"workload": HEADLINE, "desc": w.describe(), "launch_ms": round(launch_ms, 4),
+                         "TFLOP/s": round(achieved, 2),
+                         "frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4)})
+        result["sweep"] = sweep
+
+        tot, pl = bench_unfused(ea, w, 5, 2)
+        um = sum(pl) / len(pl)
+        s_bytes = w.B * w.H * w.N * w.N * 2
+        io_bytes = 4 * w.B * w.H * w.N * w.d * 2 + 4 * w.B * w.H * w.N
+        alg = 4 * s_bytes + io_bytes
+        result["unfused"] = {"ms": round(um, 3), "algorithmic_bytes": alg,
+                             "GB/s": round(alg / (um * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(alg / (um * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "TFLOP/s": round(w.flops / (um * 1e-3) / 1e12, 2),
+                             "fused_speedup": round(um / launch_ms, 2)}
+        log(f"[bench] unfused: {um:.3f} ms, {result['unfused']['GB/s']} GB/s")
+
+        if not args.no_cpu:
+            log("[bench] timing the CPU oracle on a bounded sample")
+            result["cpu_baseline"] = cpu_baseline(w)
+            log(f"[bench] cpu: {result['cpu_baseline']['value']:.6f} TFLOP/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
