@@ -63,6 +63,23 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16-byte load from a buffer straight into LDS (no VGPR staging).  Lane l's
+// 16 bytes land at lds_wave_base + 16*l; the base must be wave-uniform.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, off,
+                                             0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element
+// (j % 4) of the 4-element vectors addressed by lanes j/4, j/4+4, j/4+8 and
+// j/4+12 of its group (a 16x4 -> 4x16 transpose of 16-bit elements).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats -> two bf16 (round to nearest even) packed low/high in one word.
