@@ -214,7 +214,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "kernel": "attn::fwd_bf16::kernel<128, false, 8, 64, true>",
                      "avg_launch_ms": round(launch_ms, 4),
                      "flop_per_launch": w.flops},
     }

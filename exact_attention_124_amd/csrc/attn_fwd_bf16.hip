@@ -4,10 +4,10 @@
 // It", section "The fix: tiling and fusion, never touch HBM"; "Attention Is
 // Memory-Bound, and Nobody Noticed for Five Years", the fused-path paragraphs):
 // one workgroup owns a block of query rows, streams the K/V rows of its
-// (batch, head) slice through LDS in tiles of 64, and per tile computes the
-// scores, updates a running row maximum and row sum (the online softmax), and
-// adds the probability-weighted values into an fp32 accumulator.  Only O and
-// the log-sum-exp leave the chip; the N x N score matrix never exists.
+// (batch, head) slice through LDS in tiles of BC keys, and per tile computes
+// the scores, updates a running row maximum and row sum (the online softmax),
+// and adds the probability-weighted values into an fp32 accumulator.  Only O
+// and the log-sum-exp leave the chip; the N x N score matrix never exists.
 //
 // Mapping to CDNA4:
 //  * WAVES waves x 32 query rows.  Each wave computes S^T = K Q^T on the
@@ -20,18 +20,17 @@
 //    query, so rescaling it is a per-lane scalar multiply.
 //  * Q stays in VGPRs for the whole kernel.  K and V tiles go from HBM
 //    straight into LDS (buffer_load ... lds, 16 bytes per lane, no VGPR
-//    staging), row-major with a 16-byte XOR swizzle against bank conflicts,
-//    double-buffered so tile j+1 lands while tile j is computed.  K feeds the
-//    first product with ds_read_b128; the V^T operand of the second product is
-//    read from row-major V with ds_read_b64_tr_b16 (LDS transpose read).
-//  * Software pipelining (PIPE): K runs one tile ahead of V, so the score
-//    MFMAs of tile j+1 are issued before the softmax of tile j and execute on
-//    the matrix unit while the vector unit exponentiates.
-//  * Lazy rescaling (LAZY): the running maximum is only moved (and the
-//    accumulator rescaled) when some row of the wave exceeds it by more than
-//    2^8; otherwise the stale maximum is kept.  O and the row sum share the
-//    same reference maximum, so O = acc / l is unchanged; the probabilities
-//    stay below 2^8, well inside fp32 and bf16 range.
+//    staging), double-buffered so tile j+1 lands while tile j is computed.
+//    K feeds the first product with ds_read_b128; the V^T operand of the
+//    second product comes from ds_read_b64_tr_b16 (LDS transpose read).
+//  * KAHEAD: K runs one tile ahead of V, so the score MFMAs of tile j+1 are
+//    issued before the softmax of tile j and execute on the matrix unit while
+//    the vector unit exponentiates.
+//  * Lazy rescaling: the running maximum is only moved (and the accumulator
+//    rescaled) when some row of the wave exceeds it by more than 2^8;
+//    otherwise the stale maximum is kept.  O and the row sum share the same
+//    reference maximum, so O = acc / l is unchanged; the probabilities stay
+//    below 2^8, well inside fp32 and bf16 range.
 //  * exp is exp2 with scale*log2(e) folded into one FMA; causal tiles above
 //    the diagonal are never loaded; causal query blocks run heaviest first;
 //    block ids are remapped so one head's query blocks share an XCD's L2.
@@ -50,39 +49,65 @@ struct Params {
     float scale_log2;  // scale * log2(e)
 };
 
-template <int D, int WAVES>
+template <int D, int WAVES, int BC_>
 struct Tile {
     static constexpr int BR = 32 * WAVES;   // query rows per workgroup
-    static constexpr int BC = 64;           // keys per tile
+    static constexpr int BC = BC_;          // keys per tile
+    static constexpr int NB = BC / 32;      // 32-key blocks per tile
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int CH = D / 8;        // 16-byte chunks per K/V row
     static constexpr int TILE = BC * D;     // elements per K or V tile
-    static constexpr int LOADS = BC * CH / 64;          // wave-loads (1 KB) per tile
+    static constexpr int LOADS = BC * D / 512;  // wave-loads (1 KiB) per tile
     static constexpr int LOADS_PER_WAVE = LOADS / WAVES;
-    static_assert(LOADS % WAVES == 0, "tile loads must split evenly over waves");
-    static constexpr int LDS_ELEMS = 4 * TILE;           // K[2], V[2]
+    static_assert(BC % 32 == 0 && LOADS % WAVES == 0, "tile loads must split evenly over waves");
+    static constexpr int LDS_ELEMS = 4 * TILE;  // K[2], V[2]
 };
 
-// 16-byte-chunk XOR swizzles of the row-major LDS tiles.  K rows are read as
-// 32 rows x one chunk per half-wave (MFMA A operand); V rows are read by the
-// transpose loads as 4 rows x 4 chunks per 16 lanes.  Rows of 256 B (d=128)
-// or 128 B (d=64) alias onto the same banks without a swizzle.
+// LDS layout of the K and V tiles: key rows of D elements with a 16-byte XOR
+// swizzle against bank conflicts.  The HBM -> LDS loads put lane l's 16 bytes
+// at slot 16*l of the wave's 1 KiB block and may fetch any 16 bytes of the
+// tile, so src(c) names the tile bytes that land in LDS chunk c (a row-major
+// chunk, swizzled within its row); the read functions give each lane's element
+// offset for an MFMA operand.  Rows of 256 B (d=128) or 128 B (d=64) alias
+// onto the same banks without the swizzle.  (An "operand order" layout whose
+// operand reads are contiguous per quarter-wave was measured slower: its
+// HBM -> LDS fetches scatter 16-byte pieces over 32 rows per wave-load.)
 template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
+struct Layout {
+    __device__ static __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+    __device__ static __forceinline__ uint32_t k_src(int c) {
+        const int row = c / (D / 8), pc = c % (D / 8);
+        return (uint32_t)(row * D + 8 * (pc ^ k_swz(row))) * 2u;
+    }
+    __device__ static __forceinline__ uint32_t v_src(int c) {
+        const int row = c / (D / 8), pc = c % (D / 8);
+        return (uint32_t)(row * D + 8 * (pc ^ v_swz(row))) * 2u;
+    }
+    // K operand (A of S^T = K Q^T) of key block blk, contraction step st:
+    // lane l reads K row 32*blk + l%32, head dims 16*st + 8*(l/32) .. +7.
+    __device__ static __forceinline__ int k_read(int st, int blk, int lane) {
+        const int r = 32 * blk + (lane & 31);
+        return r * D + 8 * ((2 * st + (lane >> 5)) ^ k_swz(r));
+    }
+    // Transpose read r (0, 1) of the V^T operand for key step st, head-dim
+    // block t: 16-lane group g covers keys 16*st + 8*r + 4*(g/2) + 0..3 and
+    // dims 32*t + 16*(g%2) + 0..15, lane i of the group 4 dims of one key.
+    __device__ static __forceinline__ int v_read(int st, int t, int r, int lane) {
+        const int tg = lane >> 4, ti = lane & 15;
+        const int key = 16 * st + 8 * r + 4 * (tg >> 1) + (ti >> 2);
+        const int dd = 32 * t + 16 * (tg & 1) + 4 * (ti & 3);
+        return key * D + 8 * ((dd >> 3) ^ v_swz(key)) + (dd & 7);
+    }
+};
 
 constexpr float kLazyThreshold = 8.0f;  // log2 units
 
-template <int D, bool CAUSAL, int WAVES, bool PIPE, bool LAZY>
+template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kernel(Params p) {
-    using T = Tile<D, WAVES>;
-    constexpr int BR = T::BR, BC = T::BC, CH = T::CH;
+    using T = Tile<D, WAVES, BC>;
+    using L = Layout<D>;
+    constexpr int BR = T::BR, NB = T::NB;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS_ELEMS];
     uint16_t *const Kbuf = smem;                // [2][TILE]
     uint16_t *const Vbuf = smem + 2 * T::TILE;  // [2][TILE]
@@ -106,8 +131,9 @@ void kernel(Params p) {
     const auto rv = make_rsrc(p.v + slice, slice_bytes);
     const auto ro = make_rsrc(p.o + slice, slice_bytes);
 
-    const int q0 = qb * BR + wave * 32;  // first query row of this wave
-    const int qrow = q0 + l32;           // this lane's query row
+    const int r0 = qb * BR;         // first query row of this workgroup
+    const int q0 = r0 + wave * 32;  // first query row of this wave
+    const int qrow = q0 + l32;      // this lane's query row
 
     // Q fragment (B operand of S^T = K Q^T): lane holds query qrow and head
     // dims 16*s + 8*hf .. +7 for each 16-wide step s.  Rows >= N read as zero.
@@ -116,27 +142,33 @@ void kernel(Params p) {
     for (int s = 0; s < D / 16; ++s)
         qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
 
+    // Tiles 0 .. ntiles-1 are visited; tiles 0 .. nfull-1 need no mask for
+    // any row of the workgroup.
     int ntiles = (N + BC - 1) / BC;
-    if (CAUSAL) ntiles = min(ntiles, (qb * BR + BR + BC - 1) / BC);
+    int nfull = N / BC;
+    if (CAUSAL) {
+        ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+        nfull = min(nfull, (r0 + 1) / BC);
+    }
 
-    // ---- HBM -> LDS, 16 bytes per lane, swizzled row-major ----
-    // Wave-load `ins` fills LDS chunks [64*ins, 64*ins + 64): lane l writes
-    // chunk c = 64*ins + l = row * CH + physical chunk.
+    // ---- HBM -> LDS, 16 bytes per lane ----
+    // Wave-load `ins` fills LDS chunks [64*ins, 64*ins + 64); lane l writes
+    // chunk 64*ins + l.  Tiles past the end of the slice read as zero (buffer
+    // bounds), so loads need no guard.
     uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
 #pragma unroll
     for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
         const int c = (wave + WAVES * n) * 64 + lane;
-        const int row = c / CH, pc = c % CH;
-        k_off[n] = (uint32_t)(row * D + 8 * (pc ^ k_swz<D>(row))) * 2u;
-        v_off[n] = (uint32_t)(row * D + 8 * (pc ^ v_swz<D>(row))) * 2u;
+        k_off[n] = L::k_src(c);
+        v_off[n] = L::v_src(c);
     }
-    auto load_k = [&](int tile, int buf) {
+    auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
         const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
 #pragma unroll
         for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
             buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
     };
-    auto load_v = [&](int tile, int buf) {
+    auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
         const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
 #pragma unroll
         for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
@@ -144,37 +176,28 @@ void kernel(Params p) {
     };
 
     // ---- per-wave compute pieces ----
-    // K operand: row (32*blk + l32), logical chunk 2*st + hf.
-    auto scores = [&](int buf, f32x16 &s0, f32x16 &s1) {  // S^T = K_tile Q^T
+    // S^T = K_tile Q^T, one 32x32 accumulator per 32-key block.
+    auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
         const uint16_t *Ks = Kbuf + buf * T::TILE;
-        s0 = f32x16{};
-        s1 = f32x16{};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            const int r0 = l32, r1 = 32 + l32;
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(Ks + r0 * D + 8 * ((2 * st + hf) ^ k_swz<D>(r0)));
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(Ks + r1 * D + 8 * ((2 * st + hf) ^ k_swz<D>(r1)));
-            s0 = mfma32(a0, qf[st], s0);
-            s1 = mfma32(a1, qf[st], s1);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                s[b] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, b, lane)), qf[st], s[b]);
         }
     };
-    auto tile_active = [&](int j) { return !CAUSAL || j * BC <= q0 + 31; };
+    // Causal: a tile with no key <= the wave's last row is skipped by the wave.
+    auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
 
-    // V^T operand for key step st and head-dim block t, via two transpose
-    // reads: lane (group g = lane/16, i = lane%16) addresses key
-    // 16*st + 8*r + 4*(g/2) + i/4 and head dims 32*t + 16*(g%2) + 4*(i%4),
-    // so lane l receives head dim 32*t + l%32 at keys
+    // V^T operand for key step st and head-dim block t from two transpose
+    // reads: lane l receives head dim 32*t + l%32 at keys
     // {16*st + 4*(l/32) + 0..3} (r = 0) and {16*st + 8 + 4*(l/32) + 0..3}
-    // (r = 1): the key order of the score accumulator's lane halves.
-    const int tg = lane >> 4, ti = lane & 15;
-    const int v_key = 4 * (tg >> 1) + (ti >> 2);     // + 16*st + 8*r
-    const int v_dim = 16 * (tg & 1) + 4 * (ti & 3);  // + 32*t
-    auto v_operand = [&](const uint16_t *Vs, int st, int t) {
-        const int k0 = 16 * st + v_key, k1 = k0 + 8;
-        const int dd = 32 * t + v_dim;
-        const uint16_t *p0 = Vs + k0 * D + 8 * ((dd >> 3) ^ v_swz<D>(k0)) + (dd & 7);
-        const uint16_t *p1 = Vs + k1 * D + 8 * ((dd >> 3) ^ v_swz<D>(k1)) + (dd & 7);
-        const i16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p1);
+    // (r = 1) -- the key order of the score accumulator's lane halves.
+    auto v_operand = [&](const uint16_t *Vs, int st, int t) __attribute__((always_inline)) {
+        const i16x4 lo = lds_read_tr16(Vs + L::v_read(st, t, 0, lane));
+        const i16x4 hi = lds_read_tr16(Vs + L::v_read(st, t, 1, lane));
         const i16x4 w[2] = {lo, hi};
         return __builtin_bit_cast(bf16x8, w);
     };
@@ -186,86 +209,93 @@ void kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
-    // Softmax of one score tile and the P*V update.
-    auto consume = [&](int j, int vb, f32x16 &s0, f32x16 &s1) {
-        const int key0 = j * BC;
-        // Mask keys past the end of the sequence and, if causal, past the query.
-        if ((CAUSAL && key0 + BC - 1 > q0) || key0 + BC > N) {
+    // Online softmax of score tile j: probabilities (bf16, B operand of the
+    // P*V product, pb[2b], pb[2b+1] for key block b) relative to the running
+    // reference maximum; the output accumulator is rescaled when it moves.
+    auto softmax = [&](int j, f32x16 (&s)[NB], bf16x8 (&pb)[2 * NB], bool masked) __attribute__((always_inline)) {
+        if (masked) {  // keys past the end of the sequence and, if causal, past the query
             const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (kk > lim) s0[r] = -INFINITY;
-                if (kk + 32 > lim) s1[r] = -INFINITY;
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (kk > lim) s[b][r] = -INFINITY;
+                }
             }
         }
-        float mx = fmaxf(s0[0], s1[0]);
+        float mx = s[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
         mx = pair_max(mx) * c;  // c > 0, so scaling commutes with max
-        bool move;
-        if (LAZY) move = __builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0;
-        else move = true;
-        float alpha = 1.f;
-        if (move) {
+        // The reference maximum moves only when some row of the wave exceeds
+        // it by more than 2^kLazyThreshold.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
             const float m_new = fmaxf(m_run, mx);
             const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            alpha = fast_exp2(m_run - m_safe);
+            const float alpha = fast_exp2(m_run - m_safe);
             m_run = m_safe;
-        }
-        const float m_use = m_run;
-        bf16x8 pb[4];
-        float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p0 = fast_exp2(fmaf(s0[r], c, -m_use));
-            const float p1 = fast_exp2(fmaf(s1[r], c, -m_use));
-            rs0 += p0;
-            rs1 += p1;
-            pb[r >> 3][r & 7] = (__bf16)p0;
-            pb[2 + (r >> 3)][r & 7] = (__bf16)p1;
-        }
-        if (move) {
             l_run *= alpha;
 #pragma unroll
             for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
         }
-        l_run += rs0 + rs1;
-        // O^T += V_j^T P^T.
-        const uint16_t *Vs = Vbuf + vb * T::TILE;
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
+                const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
+                rs0 += p0;
+                rs1 += p1;
+                pb[2 * b + (r >> 3)][r & 7] = (__bf16)p0;
+                pb[2 * b + (r >> 3)][(r & 7) + 1] = (__bf16)p1;
+            }
+        }
+        l_run += rs0 + rs1;
+    };
+    // O^T += V_tile^T P^T.
+    auto pv = [&](int buf, const bf16x8 (&pb)[2 * NB]) __attribute__((always_inline)) {
+        const uint16_t *Vs = Vbuf + buf * T::TILE;
+#pragma unroll
+        for (int st = 0; st < BC / 16; ++st) {
 #pragma unroll
             for (int t = 0; t < D / 32; ++t) acc[t] = mfma32(v_operand(Vs, st, t), pb[st], acc[t]);
         }
     };
 
-    if (PIPE) {
+    if constexpr (KAHEAD) {
         // During iteration j the LDS holds K(j+1) and V(j); K(j+2) and V(j+1)
-        // are in flight.
+        // are in flight, into the buffers K(j) and V(j-1) have vacated.
         load_k(0, 0);
         load_v(0, 0);
         if (ntiles > 1) load_k(1, 1);
         wait_vmem();
         __syncthreads();
-        f32x16 sa0, sa1, sb0, sb1;
-        if (tile_active(0)) scores(0, sa0, sa1);
-        auto step = [&](int j, f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1) {
+        f32x16 sa[NB], sb[NB];
+        if (active(0)) scores(0, sa);
+        auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
             if (j + 2 < ntiles) load_k(j + 2, j & 1);
             if (j + 1 < ntiles) {
                 load_v(j + 1, (j + 1) & 1);
-                if (tile_active(j + 1)) scores((j + 1) & 1, n0, n1);
+                if (active(j + 1)) scores((j + 1) & 1, nxt);
             }
-            if (tile_active(j)) consume(j, j & 1, c0, c1);
+            if (active(j)) {
+                bf16x8 pb[2 * NB];
+                softmax(j, cur, pb, j >= nfull);
+                pv(j & 1, pb);
+            }
             wait_vmem();
             __syncthreads();
         };
         int j = 0;
         for (; j + 1 < ntiles; j += 2) {
-            step(j, sa0, sa1, sb0, sb1);
-            step(j + 1, sb0, sb1, sa0, sa1);
+            step(j, sa, sb);
+            step(j + 1, sb, sa);
         }
-        if (j < ntiles) step(j, sa0, sa1, sb0, sb1);
+        if (j < ntiles) step(j, sa, sb);
     } else {
         load_k(0, 0);
         load_v(0, 0);
@@ -277,10 +307,12 @@ void kernel(Params p) {
                 load_k(j + 1, buf ^ 1);
                 load_v(j + 1, buf ^ 1);
             }
-            if (tile_active(j)) {
-                f32x16 s0, s1;
-                scores(buf, s0, s1);
-                consume(j, buf, s0, s1);
+            if (active(j)) {
+                f32x16 s[NB];
+                bf16x8 pb[2 * NB];
+                scores(buf, s);
+                softmax(j, s, pb, j >= nfull);
+                pv(buf, pb);
             }
             wait_vmem();
             __syncthreads();
@@ -305,9 +337,9 @@ void kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL, int WAVES, bool PIPE, bool LAZY>
+template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
 hipError_t launch(const FwdArgs &a, hipStream_t s) {
-    using T = Tile<D, WAVES>;
+    using T = Tile<D, WAVES, BC>;
     Params p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
@@ -318,28 +350,29 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.nqb = (a.N + T::BR - 1) / T::BR;
     p.scale_log2 = a.scale * kLog2e;
     const unsigned blocks = (unsigned)a.BH * (unsigned)p.nqb;
-    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, PIPE, LAZY>), dim3(blocks), dim3(T::THREADS), 0, s, p);
+    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace fwd_bf16
 
 #ifndef ATTN_FWD_BF16_NO_DEFAULT_LAUNCHER
-// 8 waves (256 query rows) per workgroup share each K/V tile; when that leaves
-// fewer than four workgroups per CU, 4 waves (128 rows, two workgroups per CU)
-// keep the chip busier.
-hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
+// 8 waves (256 query rows) per workgroup share each K/V tile and run the
+// K-ahead pipeline.  4 waves (128 rows, two workgroups per CU, plain loop)
+// are used when 8-wave workgroups would leave fewer than four per CU, and for
+// causal sequences up to 4096, where the waves of a 256-row block differ by up
+// to 3.5 tiles of causal work and the shorter block wastes less of it.
+template <int D, bool CAUSAL>
+static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     using namespace fwd_bf16;
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
-    const bool wide = blocks8 >= 4 * 256;
-    if (a.d == 128) {
-        if (a.causal)
-            return wide ? launch<128, true, 8, true, true>(a, s) : launch<128, true, 4, false, true>(a, s);
-        return wide ? launch<128, false, 8, true, true>(a, s) : launch<128, false, 4, false, true>(a, s);
-    }
-    if (a.causal)
-        return wide ? launch<64, true, 8, true, true>(a, s) : launch<64, true, 4, false, true>(a, s);
-    return wide ? launch<64, false, 8, true, true>(a, s) : launch<64, false, 4, false, true>(a, s);
+    const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.N <= 4096);
+    return wide ? launch<D, CAUSAL, 8, 64, true>(a, s) : launch<D, CAUSAL, 4, 64, false>(a, s);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {
+    if (a.d == 128) return a.causal ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
+    return a.causal ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
 }
 #endif
 
