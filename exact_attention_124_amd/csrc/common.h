@@ -78,20 +78,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
 
-// Empty asm that reads and rewrites x: the value must exist at this point of
-// the instruction stream, and the code that produced it cannot be moved past.
-__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
-
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-// vmcnt(N): at most N vector memory operations of this wave still in flight
-// (they complete in issue order, so the oldest ones are done).
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-    static_assert(N >= 0 && N < 16, "vmcnt field is 4 bits here");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats -> two bf16 (round to nearest even) packed low/high in one word.
