@@ -24,20 +24,24 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "attn_oracle.c")
+_SRCS = [os.path.join(_HERE, "attn_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
 
+def _stale() -> bool:
+    return not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(s) for s in _SRCS)
+
+
 def build(force: bool = True) -> str:
-    """Compile ``attn_oracle.c`` into ``liboracle.so`` with gcc (fp64, no FMA
-    contraction, OpenMP over rows).  Returns the library path."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    """Compile the oracle C sources into ``liboracle.so`` with gcc (fp64, no
+    FMA contraction, OpenMP over rows).  Returns the library path."""
+    if not force and not _stale():
         return _LIB
     tmp = _LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", *_SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -47,7 +51,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if _stale():
         build(force=True)
     lib = ctypes.CDLL(_LIB)
     lib.oracle_attn_f64.restype = ctypes.c_int
@@ -57,6 +61,15 @@ def _load():
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,      # S N d
         ctypes.c_double, ctypes.c_int,                       # scale causal
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,       # rows n_rows threads
+    ]
+    lib.oracle_attn_bwd_f64.restype = ctypes.c_int
+    lib.oracle_attn_bwd_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,  # q k v dout
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,                   # dq dk dv
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,                      # S N d
+        ctypes.c_double, ctypes.c_int,                                       # scale causal
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,    # qrows n_q krows n_k
+        ctypes.c_int,                                                        # threads
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
@@ -106,3 +119,40 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None, threads: i
     if rc != 0:
         raise RuntimeError(f"oracle_attn_f64 failed with code {rc}")
     return o.reshape(*lead, R, d), lse.reshape(*lead, R)
+
+
+def _index(idx):
+    if idx is None:
+        return None
+    return np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1))
+
+
+def attention_backward(q, k, v, dout, scale: float, causal: bool = False, rows=None, keys=None,
+                       threads: int = 0):
+    """Exact gradient of attention in fp64 for an upstream gradient ``dout``.
+
+    ``q``, ``k``, ``v``, ``dout``: arrays of shape ``[..., N, d]``.  ``rows``:
+    optional query-row indices for ``dq``; ``keys``: optional key indices for
+    ``dk`` and ``dv`` (the same indices in every slice).  Returns
+    ``(dq, dk, dv)`` shaped ``[..., Rq, d]``, ``[..., Rk, d]``, ``[..., Rk, d]``.
+    """
+    q64, k64, v64, g64 = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    if not (q64.shape == k64.shape == v64.shape == g64.shape) or q64.ndim < 2:
+        raise ValueError("q, k, v, dout must share one shape [..., N, d]")
+    lead = q64.shape[:-2]
+    N, d = q64.shape[-2:]
+    S = int(np.prod(lead)) if lead else 1
+    qr, kr = _index(rows), _index(keys)
+    Rq = N if qr is None else qr.size
+    Rk = N if kr is None else kr.size
+    dq = np.empty((S, Rq, d), dtype=np.float64)
+    dk = np.empty((S, Rk, d), dtype=np.float64)
+    dv = np.empty((S, Rk, d), dtype=np.float64)
+    rc = _load().oracle_attn_bwd_f64(
+        q64.ctypes.data, k64.ctypes.data, v64.ctypes.data, g64.ctypes.data,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, S, N, d, float(scale), 1 if causal else 0,
+        qr.ctypes.data if qr is not None else None, Rq if qr is not None else 0,
+        kr.ctypes.data if kr is not None else None, Rk if kr is not None else 0, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd_f64 failed with code {rc}")
+    return dq.reshape(*lead, Rq, d), dk.reshape(*lead, Rk, d), dv.reshape(*lead, Rk, d)
