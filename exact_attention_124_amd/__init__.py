@@ -17,7 +17,8 @@ import os
 __all__ = [
     "AttnError", "library_path", "load_library", "attn_fwd", "attn_fwd_f32", "attn_fwd_unfused",
     "attn_fwd_unfused_f32", "attn_unfused_workspace_bytes", "attn_status_string",
-    "attn_last_hip_error", "attention", "attention_unfused", "STATUS",
+    "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
+    "attn_bwd_workspace_bytes", "attention_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,10 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
+    lib.attn_bwd.restype = I
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = SZ
     lib.attn_unfused_workspace_bytes.argtypes = [I, I, I, I]
     lib.attn_unfused_workspace_bytes.restype = SZ
     lib.attn_status_string.argtypes = [I]
@@ -82,6 +87,10 @@ def attn_last_hip_error() -> int:
 
 def attn_unfused_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
     return int(load_library().attn_unfused_workspace_bytes(B, H, N, elem_bytes))
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, N))
 
 
 # ---------------------------------------------------------------------------
@@ -186,6 +195,28 @@ def attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal=False, scale=None, s
              scale, stream)
 
 
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
+    """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv``."""
+    torch = _torch()
+    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
+    _check_qkv(o, dout, dout, torch.bfloat16)
+    if tuple(o.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d):
+        raise ValueError("o and dout must have q's shape")
+    for t in (dq, dk, dv):
+        _check_out(t, None, (B, H, N, d), torch.bfloat16, q.device)
+    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
+    if lse is None:
+        raise ValueError("lse (the forward's log-sum-exp) is required")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    st = load_library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+
+
 # ---------------------------------------------------------------------------
 # Allocating conveniences.
 # ---------------------------------------------------------------------------
@@ -220,3 +251,14 @@ def attention_unfused(q, k, v, causal=False, scale=None, stream=None, workspace=
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     return o, lse, workspace
+
+
+def attention_backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None, workspace=None):
+    """Backward of ``attention``; returns ``(dq, dk, dv)`` (bf16)."""
+    torch = _torch()
+    B, H, N, _ = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_workspace_bytes(B, H, N), 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, scale, stream)
+    return dq, dk, dv

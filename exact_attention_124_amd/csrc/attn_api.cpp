@@ -93,6 +93,31 @@ int validate_workspace(const void *q, const void *k, const void *v, const void *
     return ATTN_OK;
 }
 
+int validate_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                 const void *dq, const void *dk, const void *dv, const void *ws, size_t ws_bytes, int B, int H,
+                 int N, int d, float scale, int causal) {
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    if (st != ATTN_OK) return st;
+    if (!lse || !dout || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(ws, 16))
+        return ATTN_ERR_ALIGN;
+    const size_t need = attn_bwd_workspace_bytes(B, H, N);
+    if (need == 0 || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    // Grid of the statistics launch: 16 padded rows per workgroup.
+    if ((uint64_t)B * H * ((uint64_t)(N + 31) / 32 * 32) / 16 >= (1ull << 31)) return ATTN_ERR_SHAPE;
+    const size_t tensor = (size_t)B * H * (size_t)N * d * 2;
+    const Range in[6] = {range_of(q, tensor), range_of(k, tensor), range_of(v, tensor), range_of(o, tensor),
+                         range_of(dout, tensor), range_of(lse, (size_t)B * H * (size_t)N * sizeof(float))};
+    const Range out[4] = {range_of(dq, tensor), range_of(dk, tensor), range_of(dv, tensor), range_of(ws, need)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(out[i], in[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(out[i], out[j])) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +173,41 @@ int attn_fwd_unfused_f32(const float *q, const float *k, const float *v, float *
     if ((uint64_t)B * H * nb * nb >= (1ull << 31)) return ATTN_ERR_SHAPE;
     return finish(attn::launch_unfused_f32(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), workspace,
                                            stream));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    const unsigned __int128 npad = ((unsigned __int128)(unsigned)N + 31) / 32 * 32;
+    const unsigned __int128 n = (unsigned __int128)B * (unsigned)H * npad * 2u * 4u;
+    if (n > (unsigned __int128)SIZE_MAX) return 0;
+    return (size_t)n;
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+             void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             float scale, int causal, hipStream_t stream) {
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return ATTN_OK;
+    const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale,
+                                causal);
+    if (st != ATTN_OK) return st;
+    attn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.stats = static_cast<float *>(workspace);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.BH = B * H;
+    a.N = N;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    return finish(attn::launch_bwd_bf16(a, stream));
 }
 
 const char *attn_status_string(int status) {

@@ -1,0 +1,449 @@
+// Exact attention backward, bf16 in/out, fp32 accumulation, gfx950.
+//
+// The pages report training results of the fused method ("Attention Is
+// Memory-Bound, and Nobody Noticed for Five Years", the results paragraph:
+// faster GPT-2 training, memory linear in sequence length); its gradient is
+// the chain rule applied to the forward definition (grasp.study lesson on
+// standard self-attention, section "The Computational Steps of Standard
+// Self-Attention").  With P the softmax probabilities and dO the upstream
+// gradient:
+//
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,
+//   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Like the forward, nothing N x N reaches memory: P is recomputed tile by
+// tile from Q, K and the forward's log-sum-exp (P_ij = exp(s_ij - lse_i)).
+// Three launches on one stream, no atomics (the result is deterministic):
+//   1. stats: D_i = dO_i . O_i and lse_i * log2(e) (fp32, into the caller's
+//      workspace, rows padded to a multiple of 32 with zeros);
+//   2. dK/dV: a workgroup owns 128 keys (four waves of 32), keeps their K and
+//      V rows in VGPRs and streams 32-query tiles of Q, dO through LDS;
+//   3. dQ:   a workgroup owns 128 queries, keeps their Q and dO rows in VGPRs
+//      and streams 64-key tiles of K, V through LDS (the forward's shape).
+//
+// Orientation.  In the dK/dV kernel the products are S = Q K^T and
+// dP = dO V^T on the 32x32x16 bf16 MFMA, so a lane owns one key column and
+// its P and dS values are directly the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS.  The dQ kernel uses S^T = K Q^T, dP^T = V dO^T and
+// dQ^T += K^T dS^T, so a lane owns one query.  The transposed A operands
+// (dO^T, Q^T, K^T) come from LDS transpose reads (ds_read_b64_tr_b16).
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace bwd_bf16 {
+
+struct Params {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;   // forward log-sum-exp (natural log), [BH, N]
+    float *stats;       // workspace [BH][2][Npad]: lse * log2(e), then D; zero past N
+    int Npad;           // N rounded up to a multiple of 32
+    uint16_t *dq, *dk, *dv;
+    int N;
+    int nblk;           // blocks per slice (keys for dK/dV, queries for dQ)
+    float scale;
+    float scale_log2;   // scale * log2(e)
+};
+
+// Tiles read both row-wise (ds_read_b128 of one 16-byte chunk of 16
+// consecutive rows per quarter-wave) and transposed (ds_read_b64_tr_b16 of 4
+// consecutive rows x 32 columns per half-wave) use this XOR swizzle of the
+// 16-byte chunk index, which keeps both access patterns free of bank
+// conflicts: it differs on 16 consecutive rows (same parity rows, for the
+// 128-byte rows of d=64), and four consecutive rows land in different
+// aligned groups of four chunks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+// LDS element offset of 16-byte chunk `chunk` of tile row `row`.
+template <int D>
+__device__ __forceinline__ int at(int row, int chunk) {
+    return row * D + 8 * (chunk ^ swz<D>(row));
+}
+// Tile byte offset that LDS chunk c (row-major chunk order) takes its 16
+// bytes from, for the HBM -> LDS loads.
+template <int D>
+__device__ __forceinline__ uint32_t src_off(int c) {
+    const int row = c / (D / 8), pc = c % (D / 8);
+    return (uint32_t)(row * D + 8 * (pc ^ swz<D>(row))) * 2u;
+}
+// A operand [32 rows x 16 columns] for contraction step st from rows
+// rbase.. of a tile: lane l reads row rbase + l%32, columns 16*st + 8*(l/32).
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t *tile, int rbase, int st, int lane) {
+    const int r = rbase + (lane & 31);
+    return *reinterpret_cast<const bf16x8 *>(tile + at<D>(r, 2 * st + (lane >> 5)));
+}
+// Transposed A operand [32 columns x 16 rows] for row step st (rows
+// 16*st ..) and column block t (columns 32*t ..): lane l receives column
+// 32*t + l%32 at rows {16*st + 4*(l/32) + 0..3, 16*st + 8 + 4*(l/32) + 0..3},
+// the row order of a 32x32 accumulator's lane halves.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int st, int t, int lane) {
+    const int tg = lane >> 4, ti = lane & 15;
+    const int dd = 32 * t + 16 * (tg & 1) + 4 * (ti & 3);
+    i16x4 h[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 16 * st + 8 * r + 4 * (tg >> 1) + (ti >> 2);
+        h[r] = lds_read_tr16(tile + row * D + 8 * ((dd >> 3) ^ swz<D>(row)) + (dd & 7));
+    }
+    return __builtin_bit_cast(bf16x8, h);
+}
+
+// Store a [D x 32] accumulator pair (rows = columns of the output row,
+// lane = output row) as one bf16 row per lane, multiplied by `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mul, __amdgpu_buffer_rsrc_t r,
+                                           int row, int hf) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[t][4 * g] * mul, acc[t][4 * g + 1] * mul);
+            w[1] = pack_bf16x2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
+            buf_store8(w, r, (uint32_t)(row * D + 32 * t + 8 * g + 4 * hf) * 2u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 1. Row statistics: lse_i * log2(e) and D_i = dO_i . O_i, 16 lanes per row,
+//    over the padded rows of every slice (zeros past N).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout,
+                                                    const float *__restrict__ lse, float *__restrict__ stats, int N,
+                                                    int Npad, long long prow_total) {
+    constexpr int PER = D / 16;  // elements per lane
+    const long long prow = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);  // padded row
+    const int l16 = threadIdx.x & 15;
+    const long long bh = prow / Npad;
+    const int r = (int)(prow - bh * Npad);
+    const bool live = prow < prow_total && r < N;
+    const long long row = bh * N + r;
+    float acc = 0.f;
+    if (live) {
+        const uint16_t *po = o + row * D + l16 * PER;
+        const uint16_t *pd = dout + row * D + l16 * PER;
+        uint32_t wo[PER / 2], wd[PER / 2];
+        if (PER == 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(po), b = *reinterpret_cast<const u32x4 *>(pd);
+#pragma unroll
+            for (int i = 0; i < PER / 2; ++i) { wo[i] = a[i]; wd[i] = b[i]; }
+        } else {
+            const u32x2 a = *reinterpret_cast<const u32x2 *>(po), b = *reinterpret_cast<const u32x2 *>(pd);
+#pragma unroll
+            for (int i = 0; i < PER / 2; ++i) { wo[i] = a[i]; wd[i] = b[i]; }
+        }
+#pragma unroll
+        for (int i = 0; i < PER / 2; ++i) {
+            acc = fmaf(bf16_lo(wo[i]), bf16_lo(wd[i]), acc);
+            acc = fmaf(bf16_hi(wo[i]), bf16_hi(wd[i]), acc);
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (prow < prow_total && l16 == 0) {
+        float *st = stats + bh * 2 * Npad;
+        st[r] = live ? lse[row] * kLog2e : 0.f;
+        st[Npad + r] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV.  Four waves x 32 keys; 32-query tiles of Q and dO stream
+//    through double-buffered LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dkdv_kernel(Params p) {
+    constexpr int WAVES = 4, BK = 32 * WAVES, BQ = 32;
+    constexpr int QT = BQ * D;                       // elements per Q or dO tile
+    constexpr int LPW = QT / 512 / WAVES;            // wave-loads per wave per tile
+    static_assert(LPW >= 1 && (QT / 512) % WAVES == 0, "tile loads must split evenly");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * QT];
+    uint16_t *const Qbuf = smem;             // [2][QT]
+    uint16_t *const Obuf = smem + 2 * QT;    // [2][QT] (dO)
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nblk;
+    const int kb = logical - bh * p.nblk;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int N = p.N;
+
+    const size_t slice = (size_t)bh * N * D;
+    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+    const auto rq = make_rsrc(p.q + slice, slice_bytes);
+    const auto rk = make_rsrc(p.k + slice, slice_bytes);
+    const auto rv = make_rsrc(p.v + slice, slice_bytes);
+    const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
+    const auto rdk = make_rsrc(p.dk + slice, slice_bytes);
+    const auto rdv = make_rsrc(p.dv + slice, slice_bytes);
+    const float *st = p.stats + (size_t)bh * 2 * p.Npad;
+    const auto rlse = make_rsrc(st, (uint32_t)p.Npad * 4u);
+    const auto rdl = make_rsrc(st + p.Npad, (uint32_t)p.Npad * 4u);
+
+    const int k0 = kb * BK + wave * 32;  // first key of this wave
+    const int key = k0 + l32;            // this lane's key
+
+    // Resident K and V (B operands of S = Q K^T and dP = dO V^T): lane holds
+    // key `key`, columns 16*st + 8*hf .. +7.  Keys >= N read as zero.
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        const uint32_t off = (uint32_t)(key * D + 16 * st + 8 * hf) * 2u;
+        kf[st] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+        vf[st] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+
+    const int nqt = (N + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? (kb * BK) / BQ : 0;  // first query tile that sees any key of the block
+    auto active = [&](int i) __attribute__((always_inline)) { return !CAUSAL || i * BQ + BQ - 1 >= k0; };
+
+    uint32_t ld_off[LPW];
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
+    auto load_tile = [&](int i, int buf) __attribute__((always_inline)) {
+        const uint32_t base = (uint32_t)(i * BQ * D) * 2u;
+#pragma unroll
+        for (int n = 0; n < LPW; ++n) {
+            buf_load16_lds(rq, base + ld_off[n], Qbuf + buf * QT + (wave + WAVES * n) * 512);
+            buf_load16_lds(rdo, base + ld_off[n], Obuf + buf * QT + (wave + WAVES * n) * 512);
+        }
+    };
+
+    const float c = p.scale_log2;
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+        dk[t] = f32x16{};
+        dv[t] = f32x16{};
+    }
+
+    if (t0 < nqt) {
+        load_tile(t0, 0);
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int i = t0; i < nqt; ++i) {
+        const int buf = (i - t0) & 1;
+        if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
+        if (active(i)) {
+            const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
+            // Statistics of this lane's 16 query rows 8*g + 4*hf + 0..3
+            // (within the padded rows, so every 16-byte load is in range).
+            f32x4 lse4[4], dl4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t off = (uint32_t)(i * BQ + 8 * g + 4 * hf) * 4u;
+                lse4[g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
+                dl4[g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
+            }
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                s = mfma32(row_operand<D>(Qs, 0, st, lane), kf[st], s);
+                dp = mfma32(row_operand<D>(Os, 0, st, lane), vf[st], dp);
+            }
+            // P = exp(scale*s - lse), dS = P (dP - D); masked entries are 0.
+            const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
+            bf16x8 pb[2], db[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float lse2 = lse4[r >> 2][r & 3];
+                float pr = fast_exp2(fmaf(s[r], c, -lse2));
+                if (edge) {
+                    const int qi = i * BQ + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (qi >= N || (CAUSAL && key > qi)) pr = 0.f;
+                }
+                const float ds = pr * (dp[r] - dl4[r >> 2][r & 3]);
+                pb[r >> 3][r & 7] = (__bf16)pr;
+                db[r >> 3][r & 7] = (__bf16)ds;
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
+#pragma unroll
+            for (int st = 0; st < BQ / 16; ++st) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) {
+                    dv[t] = mfma32(tr_operand<D>(Os, st, t, lane), pb[st], dv[t]);
+                    dk[t] = mfma32(tr_operand<D>(Qs, st, t, lane), db[st], dk[t]);
+                }
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+
+    if (key < N) {
+        store_rows<D>(dk, p.scale, rdk, key, hf);
+        store_rows<D>(dv, 1.f, rdv, key, hf);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ.  Four waves x 32 queries; 64-key tiles of K and V stream through
+//    double-buffered LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(Params p) {
+    constexpr int WAVES = 4, BR = 32 * WAVES, BC = 64;
+    constexpr int KT = BC * D;
+    constexpr int LPW = KT / 512 / WAVES;
+    static_assert(LPW >= 1 && (KT / 512) % WAVES == 0, "tile loads must split evenly");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * KT];
+    uint16_t *const Kbuf = smem;           // [2][KT]
+    uint16_t *const Vbuf = smem + 2 * KT;  // [2][KT]
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / p.nblk;
+    int qb = logical - bh * p.nblk;
+    if (CAUSAL) qb = p.nblk - 1 - qb;  // longest rows first
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int N = p.N;
+
+    const size_t slice = (size_t)bh * N * D;
+    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+    const auto rq = make_rsrc(p.q + slice, slice_bytes);
+    const auto rk = make_rsrc(p.k + slice, slice_bytes);
+    const auto rv = make_rsrc(p.v + slice, slice_bytes);
+    const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
+    const auto rdq = make_rsrc(p.dq + slice, slice_bytes);
+
+    const int r0 = qb * BR;
+    const int q0 = r0 + wave * 32;
+    const int qrow = q0 + l32;
+
+    // Resident Q and dO (B operands of S^T = K Q^T and dP^T = V dO^T).
+    bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        const uint32_t off = (uint32_t)(qrow * D + 16 * st + 8 * hf) * 2u;
+        qf[st] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+        of[st] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+    }
+    const bool live = qrow < N;
+    const float *stq = p.stats + (size_t)bh * 2 * p.Npad;
+    const float lse2 = live ? stq[qrow] : 0.f;
+    const float dlt = live ? stq[p.Npad + qrow] : 0.f;
+
+    int ntiles = (N + BC - 1) / BC;
+    int nfull = N / BC;
+    if (CAUSAL) {
+        ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+        nfull = min(nfull, (r0 + 1) / BC);
+    }
+    auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
+
+    uint32_t ld_off[LPW];
+#pragma unroll
+    for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
+    auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
+        const uint32_t base = (uint32_t)(j * BC * D) * 2u;
+#pragma unroll
+        for (int n = 0; n < LPW; ++n) {
+            buf_load16_lds(rk, base + ld_off[n], Kbuf + buf * KT + (wave + WAVES * n) * 512);
+            buf_load16_lds(rv, base + ld_off[n], Vbuf + buf * KT + (wave + WAVES * n) * 512);
+        }
+    };
+
+    const float c = p.scale_log2;
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) dq[t] = f32x16{};
+
+    load_tile(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
+        if (active(j)) {
+            const uint16_t *Ks = Kbuf + buf * KT, *Vs = Vbuf + buf * KT;
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                s[b] = f32x16{};
+                dp[b] = f32x16{};
+            }
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    s[b] = mfma32(row_operand<D>(Ks, 32 * b, st, lane), qf[st], s[b]);
+                    dp[b] = mfma32(row_operand<D>(Vs, 32 * b, st, lane), of[st], dp[b]);
+                }
+            }
+            const bool masked = j >= nfull;
+            const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+            bf16x8 db[4];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr = fast_exp2(fmaf(s[b][r], c, -lse2));
+                    if (masked) {
+                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (kk > lim) pr = 0.f;
+                    }
+                    db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] - dlt));
+                }
+            }
+            // dQ^T += K^T dS^T (scale applied at the end).
+#pragma unroll
+            for (int st = 0; st < BC / 16; ++st) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(tr_operand<D>(Ks, st, t, lane), db[st], dq[t]);
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    }
+    if (live) store_rows<D>(dq, p.scale, rdq, qrow, hf);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs &a, hipStream_t s) {
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<const uint16_t *>(a.o);
+    p.dout = static_cast<const uint16_t *>(a.dout);
+    p.lse = a.lse;
+    p.stats = a.stats;
+    p.Npad = (a.N + 31) / 32 * 32;
+    p.dq = static_cast<uint16_t *>(a.dq);
+    p.dk = static_cast<uint16_t *>(a.dk);
+    p.dv = static_cast<uint16_t *>(a.dv);
+    p.N = a.N;
+    p.scale = a.scale;
+    p.scale_log2 = a.scale * kLog2e;
+    const long long prows = (long long)a.BH * p.Npad;
+    hipLaunchKernelGGL((stats_kernel<D>), dim3((unsigned)((prows + 15) / 16)), dim3(256), 0, s, p.o, p.dout,
+                       p.lse, p.stats, a.N, p.Npad, prows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.nblk = (a.N + 127) / 128;
+    const unsigned blocks = (unsigned)a.BH * (unsigned)p.nblk;
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(blocks), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace bwd_bf16
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
+    using namespace bwd_bf16;
+    if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+    return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+}
+
+}  // namespace attn

@@ -31,6 +31,27 @@ hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 hipError_t launch_unfused_bf16(const FwdArgs &a, void *ws, hipStream_t s);
 hipError_t launch_unfused_f32(const FwdArgs &a, void *ws, hipStream_t s);
 
+struct BwdArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *o;
+    const void *dout;
+    const float *lse;
+    float *stats;  // workspace: BH * 2 * round_up(N, 32) floats
+    void *dq;
+    void *dk;
+    void *dv;
+    int BH;
+    int N;
+    int d;
+    float scale;
+    int causal;
+};
+
+// Backward: row statistics, then dK/dV, then dQ (three launches).
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
+
 // Query-row block of the fused bf16 kernel (used for grid-size limits).
 constexpr int kFwdBlockRows = 128;
 

@@ -14,7 +14,9 @@ head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
 * converted to the working dtype with ``Tensor.to`` (round to nearest even for
   bfloat16);
 * slices to check against the oracle: ``randperm(B*H)`` from a second
-  generator seeded with ``seed + 1``.
+  generator seeded with ``seed + 1``;
+* the upstream gradient dO of the backward: float32 ``randn`` of the same
+  shape from a generator seeded with ``seed + 100``, then the working dtype.
 """
 from __future__ import annotations
 
@@ -87,6 +89,13 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0
         t = t.to(dtype)
         out.append(t.to(device) if str(device) != "cpu" else t)
     return tuple(out)
+
+
+def make_grad(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0, device="cpu"):
+    """Upstream gradient dO for the backward (see the module docstring)."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 100)
+    t = torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(dtype)
+    return t.to(device) if str(device) != "cpu" else t
 
 
 def workload_inputs(w: Workload, device="cpu"):

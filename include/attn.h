@@ -109,6 +109,37 @@ int attn_fwd_unfused_f32(const float *q, const float *k, const float *v, float *
                          int B, int H, int N, int d, float scale, int causal,
                          hipStream_t stream);
 
+/*
+ * Backward of the fused forward, bfloat16: gradients of the attention output
+ * with respect to q, k and v for an upstream gradient dout, computed the same
+ * fused way (the N x N probabilities are recomputed tile by tile from q, k and
+ * the forward's lse and never stored).  The function differentiated is the
+ * one attn_fwd computes (grasp.study lesson on standard self-attention,
+ * section "The Computational Steps of Standard Self-Attention"; the pages
+ * report the fused method's training speed in "Attention Is Memory-Bound, and
+ * Nobody Noticed for Five Years", results paragraph, but do not write out the
+ * gradient):
+ *     dV = P^T dO,   dS = P o (dO V^T - rowsum(dO o O)),
+ *     dQ = scale dS K,   dK = scale dS^T Q.
+ *   q, k, v, o, dout : const bf16 [B,H,N,d]; o and lse are attn_fwd's outputs
+ *                      for these q, k, v, scale and causal (not checked)
+ *   lse              : const float [B,H,N], required
+ *   dq, dk, dv       : bf16 [B,H,N,d] outputs (RNE from fp32)
+ *   workspace        : device buffer of at least attn_bwd_workspace_bytes()
+ *                      bytes, 16-byte aligned; holds per-row statistics
+ * Three launches on `stream`; the result is deterministic (no atomics).
+ * Checks: as attn_fwd (with dout, dq, dk, dv, lse and workspace required and
+ * aligned), workspace size (ATTN_ERR_WORKSPACE), and no output or workspace
+ * range overlapping an input range or another output (ATTN_ERR_ALIAS).
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+             int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Workspace bytes attn_bwd needs: B*H*2*round_up(N, 32)*4.  Returns 0 for
+ * non-positive arguments or on size_t overflow.  Pure host function. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char *attn_status_string(int status);
 

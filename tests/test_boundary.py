@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_unfused", "attn_fwd_unfused_f32",
                             "attn_unfused_workspace_bytes", "attn_status_string",
-                            "attn_last_hip_error"])
+                            "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -137,6 +137,50 @@ def test_unfused_validation_codes(lib, name, elem):
     assert unf(lib, name, elem=elem, ws=L - 64) == S["ATTN_ERR_ALIAS"]
     assert unf(lib, name, elem=elem, q=None) == S["ATTN_ERR_NULL"]
     assert unf(lib, name, elem=elem, N=0) == S["ATTN_OK"]
+
+
+DO, DQ, DK, DV = (A + i * GAP for i in range(6, 10))
+
+
+def bwd(lib, ws=W, ws_bytes=None, B=1, H=2, N=256, d=64, **kw):
+    if ws_bytes is None:
+        ws_bytes = B * H * 2 * ((N + 31) // 32 * 32) * 4
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, scale=0.125, causal=0)
+    args.update(kw)
+    return lib.attn_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dout"], args["dq"],
+                        args["dk"], args["dv"], ws, ws_bytes, B, H, N, d, args["scale"], args["causal"], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    import exact_attention_124_amd as ea
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1) == 2 * 32 * 4
+    assert ea.attn_bwd_workspace_bytes(2, 3, 33) == 2 * 3 * 2 * 64 * 4
+    assert ea.attn_bwd_workspace_bytes(8, 32, 8192) == 8 * 32 * 2 * 8192 * 4
+    assert ea.attn_bwd_workspace_bytes(0, 1, 1) == 0
+    assert ea.attn_bwd_workspace_bytes(1, 1, -1) == 0
+
+
+def test_bwd_validation_codes(lib):
+    S = __import__("exact_attention_124_amd").STATUS
+    # Every call below fails validation, so nothing is launched on the fake
+    # addresses (a fully valid call would enqueue kernels).
+    for name in ("q", "o", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: None}) == S["ATTN_ERR_NULL"], name
+    assert bwd(lib, ws=None) == S["ATTN_ERR_NULL"]
+    assert bwd(lib, N=0) == S["ATTN_OK"]
+    assert bwd(lib, N=-1) == S["ATTN_ERR_SHAPE"]
+    assert bwd(lib, d=96) == S["ATTN_ERR_HEAD_DIM"]
+    assert bwd(lib, scale=0.0) == S["ATTN_ERR_ARG"]
+    assert bwd(lib, causal=3) == S["ATTN_ERR_ARG"]
+    assert bwd(lib, dq=DQ + 8) == S["ATTN_ERR_ALIGN"]
+    assert bwd(lib, ws=W + 4) == S["ATTN_ERR_ALIGN"]
+    assert bwd(lib, ws_bytes=2 * 2 * 256 * 4 - 1) == S["ATTN_ERR_WORKSPACE"]
+    assert bwd(lib, dq=Q) == S["ATTN_ERR_ALIAS"]        # output over an input
+    assert bwd(lib, dk=DO + 64) == S["ATTN_ERR_ALIAS"]
+    assert bwd(lib, dv=DQ) == S["ATTN_ERR_ALIAS"]       # two outputs
+    assert bwd(lib, ws=L) == S["ATTN_ERR_ALIAS"]        # workspace over lse
+    assert bwd(lib, ws=DK + 32) == S["ATTN_ERR_ALIAS"]  # workspace over an output
+    assert bwd(lib, N=1 << 26, d=128) == S["ATTN_ERR_SHAPE"]
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
