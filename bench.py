@@ -15,7 +15,9 @@ Prints ONE JSON line.  Besides the headline value it carries:
                    workload (the host cores of this machine);
   sweep         -- the same fused forward on the other workloads;
   unfused       -- the three-launch standard path on the same workload, with
-                   its algorithmic HBM bytes per second.
+                   its algorithmic HBM bytes per second;
+  backward      -- attn_bwd (dQ, dK, dV) on the dense 8k and causal 32k
+                   workloads.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick]
 """
@@ -112,6 +114,23 @@ def bench_unfused(ea, w, steps, warmup):
     call = lambda: ea.attn_fwd_unfused(q, k, v, o, lse, ws, causal=w.causal, stream=stream)  # noqa
     total_ms, per = time_launches(call, steps, warmup, stream)
     del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return total_ms, per
+
+
+def bench_backward(ea, w, steps, warmup):
+    """Time attn_bwd (statistics, dK/dV and dQ launches) on workload `w`."""
+    import torch
+    from exact_attention_124_amd.workloads import make_grad, workload_inputs
+    q, k, v = workload_inputs(w, device="cuda")
+    g = make_grad(w.B, w.H, w.N, w.d, w.dtype, w.seed, device="cuda")
+    o, lse = ea.attention(q, k, v, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: ea.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, ws, causal=w.causal, stream=stream)  # noqa
+    total_ms, per = time_launches(call, steps, warmup, stream)
+    del q, k, v, g, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return total_ms, per
 
@@ -250,6 +269,20 @@ def main():
                              "TFLOP/s": round(w.flops / (um * 1e-3) / 1e12, 2),
                              "fused_speedup": round(um / launch_ms, 2)}
         log(f"[bench] unfused: {um:.3f} ms, {result['unfused']['GB/s']} GB/s")
+
+        bwd = []
+        for name in (HEADLINE, "causal_32k_qx8_bf16"):
+            ww = WORKLOADS[name]
+            tot, pl = bench_backward(ea, ww, 5, 2)
+            bm = sum(pl) / len(pl)
+            alg = 2.5 * ww.flops  # five products of 2*N^2*d per (b, h), halved when causal
+            bwd.append({"workload": name, "ms": round(bm, 3),
+                        "TFLOP/s": round(alg / (bm * 1e-3) / 1e12, 2),
+                        "frac_bf16_peak": round(alg / (bm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "flop_convention": "10*B*H*N^2*d (halved when causal); the kernels execute "
+                                           "14*B*H*N^2*d (S and dP are recomputed for dQ)"})
+            log(f"[bench] backward {name}: {bm:.3f} ms, {bwd[-1]['TFLOP/s']} TFLOP/s")
+        result["backward"] = bwd
 
         if not args.no_cpu:
             log("[bench] timing the CPU oracle on a bounded sample")
