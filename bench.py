@@ -179,6 +179,22 @@ def cpu_baseline(w, target_s=15.0):
             "seconds": round(secs, 3), "flop": flops}
 
 
+def n_sweep(ea):
+    """One fused and one unfused forward per sequence length, B=1 H=32 d=128
+    non-causal, then a 1 GiB copy: a profiler's per-dispatch byte counters then
+    show how each path's HBM traffic grows with N."""
+    import dataclasses
+    import torch
+    from exact_attention_124_amd.workloads import WORKLOADS
+    for N in (1024, 2048, 4096, 8192, 16384):
+        w = dataclasses.replace(WORKLOADS[HEADLINE], name=f"n_sweep_{N}", B=1, H=32, N=N)
+        bench_fused(ea, w, 1, 0)
+        bench_unfused(ea, w, 1, 0)
+        torch.cuda.synchronize()
+        log(f"[bench] n-sweep N={N} done")
+    copy_calibration(reps=2)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +204,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="only run fused and unfused once each at B=1 H=32 d=128 for N = 1k..16k "
+                         "(for HBM byte counters), plus the copy calibration")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -203,6 +222,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.n_sweep:
+        n_sweep(ea)
+        return
 
     w = WORKLOADS[HEADLINE]
     log(f"[bench] headline: {w.describe()}, warmup {args.warmup}, steps {args.steps}")
