@@ -16,7 +16,11 @@ head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
 * slices to check against the oracle: ``randperm(B*H)`` from a second
   generator seeded with ``seed + 1``;
 * the upstream gradient dO of the backward: float32 ``randn`` of the same
-  shape from a generator seeded with ``seed + 100``, then the working dtype.
+  shape from a generator seeded with ``seed + 100``, then the working dtype;
+* 8-bit inputs: the float32 ``Q``, ``K``, ``V`` above, each divided by its
+  per-tensor factor ``descale = max|x| / 448`` (float32) and converted to
+  ``torch.float8_e4m3fn`` (round to nearest even; the largest magnitude lands
+  on 448, the largest finite E4M3 value).
 """
 from __future__ import annotations
 
@@ -89,6 +93,23 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0
         t = t.to(dtype)
         out.append(t.to(device) if str(device) != "cpu" else t)
     return tuple(out)
+
+
+E4M3_MAX = 448.0
+
+
+def make_qkv_fp8(B: int, H: int, N: int, d: int, seed: int = 0, q_mult: float = 1.0, device="cpu"):
+    """8-bit Q, K, V and their float32 dequantisation factors (see the module
+    docstring): returns ``(q8, k8, v8, q_descale, k_descale, v_descale)``."""
+    qkv = make_qkv(B, H, N, d, torch.float32, seed, q_mult)
+    out, scales = [], []
+    for t in qkv:
+        amax = float(t.abs().max()) if t.numel() else 1.0
+        ds = torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32)
+        t8 = (t / ds).to(torch.float8_e4m3fn)
+        out.append(t8.to(device) if str(device) != "cpu" else t8)
+        scales.append(float(ds))
+    return (*out, *scales)
 
 
 def make_grad(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0, device="cpu"):

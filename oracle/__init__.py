@@ -121,6 +121,44 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None, threads: i
     return o.reshape(*lead, R, d), lse.reshape(*lead, R)
 
 
+# ---------------------------------------------------------------------------
+# 8-bit floating point inputs.
+# ---------------------------------------------------------------------------
+def decode_e4m3(codes) -> np.ndarray:
+    """Value of each OCP FP8 E4M3 byte as float64, written out from the format
+    definition: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 encodes subnormals m * 2^-9; the all-ones exponent with
+    all-ones mantissa (0x7F, 0xFF) is NaN and every other code is finite (no
+    infinities), so the largest value is 1.75 * 2^8 = 448.
+
+    ``codes``: uint8 array, or a torch float8_e4m3fn / uint8 tensor (read as
+    raw bytes, never converted by torch)."""
+    if hasattr(codes, "detach"):
+        import torch
+        t = codes.detach().to("cpu").contiguous()
+        if t.dtype != torch.uint8:
+            t = t.view(torch.uint8)
+        codes = t.numpy()
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    val = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, val)
+
+
+def attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float, scale: float,
+                  causal: bool = False, rows=None, threads: int = 0):
+    """Exact attention of dequantised 8-bit inputs: the inputs are
+    ``descale * decode_e4m3(code)`` per tensor (exact in fp64: a 4-bit
+    significand times an fp32 factor), then :func:`attention` in fp64."""
+    qd, kd, vd = (float(np.float32(x)) for x in (q_descale, k_descale, v_descale))
+    return attention(decode_e4m3(q8) * qd, decode_e4m3(k8) * kd, decode_e4m3(v8) * vd, scale, causal,
+                     rows=rows, threads=threads)
+
+
 def _index(idx):
     if idx is None:
         return None
