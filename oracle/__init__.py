@@ -24,7 +24,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "attn_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c")]
+_SRCS = [os.path.join(_HERE, "attn_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c"),
+         os.path.join(_HERE, "attn_probs_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
@@ -70,6 +71,13 @@ def _load():
         ctypes.c_double, ctypes.c_int,                                       # scale causal
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,    # qrows n_q krows n_k
         ctypes.c_int,                                                        # threads
+    ]
+    lib.oracle_attn_probs_f64.restype = ctypes.c_int
+    lib.oracle_attn_probs_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,   # q k w
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,      # S N d
+        ctypes.c_double, ctypes.c_int,                       # scale causal
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,       # rows n_rows threads
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
@@ -121,6 +129,27 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None, threads: i
     return o.reshape(*lead, R, d), lse.reshape(*lead, R)
 
 
+def probabilities(q, k, scale: float, causal: bool = False, rows=None, threads: int = 0):
+    """The attention weights softmax(scale * q k^T) of the selected query rows
+    (every row if ``rows`` is None), fp64, shape ``[..., R, N]``; disallowed
+    (causal) keys get 0."""
+    q64, k64 = _as_f64(q), _as_f64(k)
+    if q64.shape != k64.shape or q64.ndim < 2:
+        raise ValueError("q and k must share one shape [..., N, d]")
+    lead = q64.shape[:-2]
+    N, d = q64.shape[-2:]
+    S = int(np.prod(lead)) if lead else 1
+    r = _index(rows)
+    R = N if r is None else r.size
+    w = np.empty((S, R, N), dtype=np.float64)
+    rc = _load().oracle_attn_probs_f64(q64.ctypes.data, k64.ctypes.data, w.ctypes.data, S, N, d, float(scale),
+                                       1 if causal else 0, r.ctypes.data if r is not None else None,
+                                       R if r is not None else 0, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_probs_f64 failed with code {rc}")
+    return w.reshape(*lead, R, N)
+
+
 # ---------------------------------------------------------------------------
 # 8-bit floating point inputs.
 # ---------------------------------------------------------------------------
@@ -147,6 +176,11 @@ def decode_e4m3(codes) -> np.ndarray:
     sub = (m / 8.0) * 2.0 ** -6
     val = sign * np.where(e == 0, sub, normal)
     return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, val)
+
+
+def dequantize_fp8(t8, descale: float) -> np.ndarray:
+    """``descale * decode_e4m3(t8)`` in fp64 (exact)."""
+    return decode_e4m3(t8) * float(np.float32(descale))
 
 
 def attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float, scale: float,
