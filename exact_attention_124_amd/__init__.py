@@ -18,7 +18,7 @@ __all__ = [
     "AttnError", "library_path", "load_library", "attn_fwd", "attn_fwd_f32", "attn_fwd_unfused",
     "attn_fwd_unfused_f32", "attn_unfused_workspace_bytes", "attn_status_string",
     "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
-    "attn_bwd_workspace_bytes", "attention_backward",
+    "attn_bwd_workspace_bytes", "attention_backward", "attn_fwd_fp8", "attention_fp8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +63,8 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
+    lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P]
+    lib.attn_fwd_fp8.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
     lib.attn_bwd.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
@@ -195,6 +197,18 @@ def attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal=False, scale=None, s
              scale, stream)
 
 
+def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
+    """fp8 (e4m3) fused forward into caller-allocated bf16 ``o`` (and ``lse``)."""
+    torch = _torch()
+    B, H, N, d = _check_qkv(q, k, v, torch.float8_e4m3fn)
+    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
+    st = load_library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                                     B, H, N, d, _scale(scale, d), float(q_descale), float(k_descale),
+                                     float(v_descale), 1 if causal else 0, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
+
+
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
     """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv``."""
     torch = _torch()
@@ -231,6 +245,15 @@ def attention(q, k, v, causal=False, scale=None, stream=None):
         attn_fwd_f32(q, k, v, o, lse, causal, scale, stream)
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    return o, lse
+
+
+def attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
+    """fp8 fused forward; returns ``(o, lse)`` with ``o`` in bf16."""
+    torch = _torch()
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal, scale, stream)
     return o, lse
 
 

@@ -25,8 +25,10 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Shared checks of every forward entry point.  Returns ATTN_OK to proceed,
 // a negative value for "valid but empty" (nothing to do), or an error code.
+// in_elem / out_elem: bytes per element of q, k, v and of o.
 int validate_common(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                    int B, int H, int N, int d, float scale, int causal, size_t elem) {
+                    int B, int H, int N, int d, float scale, int causal, size_t in_elem, size_t out_elem) {
+    const size_t elem = in_elem > out_elem ? in_elem : out_elem;
     if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
     if (B == 0 || H == 0 || N == 0) return -1;  // empty: no memory is touched, NULL allowed
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
@@ -43,9 +45,9 @@ int validate_common(const void *q, const void *k, const void *v, const void *o, 
     if (BH >= (1ull << 31)) return ATTN_ERR_SHAPE;
     const uint64_t blocks = BH * (uint64_t)((N + attn::kFwdBlockRows - 1) / attn::kFwdBlockRows);
     if (blocks >= (1ull << 31)) return ATTN_ERR_SHAPE;
-    const size_t tensor = (size_t)BH * (size_t)N * (size_t)d * elem;
-    const Range rq = range_of(q, tensor), rk = range_of(k, tensor), rv = range_of(v, tensor);
-    const Range ro = range_of(o, tensor);
+    const size_t elems = (size_t)BH * (size_t)N * (size_t)d;
+    const Range rq = range_of(q, elems * in_elem), rk = range_of(k, elems * in_elem), rv = range_of(v, elems * in_elem);
+    const Range ro = range_of(o, elems * out_elem);
     if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv)) return ATTN_ERR_ALIAS;
     if (lse) {
         const Range rl = range_of(lse, (size_t)BH * (size_t)N * sizeof(float));
@@ -93,10 +95,20 @@ int validate_workspace(const void *q, const void *k, const void *v, const void *
     return ATTN_OK;
 }
 
+// fp8 forward: 1-byte q, k, v and a 2-byte o; the descale factors are
+// checked with scale (before alignment, as scale is).
+int validate_fp8(const void *q, const void *k, const void *v, const void *o, const float *lse, int B, int H,
+                 int N, int d, float scale, float qd, float kd, float vd, int causal) {
+    if (B > 0 && H > 0 && N > 0 && q && k && v && o && (d == 64 || d == 128))
+        for (float x : {qd, kd, vd})
+            if (!isfinite(x) || !(x > 0.f)) return ATTN_ERR_ARG;
+    return validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 1, 2);
+}
+
 int validate_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                  const void *dq, const void *dk, const void *dv, const void *ws, size_t ws_bytes, int B, int H,
                  int N, int d, float scale, int causal) {
-    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2, 2);
     if (st != ATTN_OK) return st;
     if (!lse || !dout || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(ws, 16))
@@ -124,7 +136,7 @@ extern "C" {
 
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
              float scale, int causal, hipStream_t stream) {
-    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2, 2);
     if (st < 0) return ATTN_OK;
     if (st != ATTN_OK) return st;
     return finish(attn::launch_fwd_bf16(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), stream));
@@ -132,10 +144,23 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 
 int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H, int N,
                  int d, float scale, int causal, hipStream_t stream) {
-    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4);
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4, 4);
     if (st < 0) return ATTN_OK;
     if (st != ATTN_OK) return st;
     return finish(attn::launch_fwd_f32(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), stream));
+}
+
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+                 float scale, float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream) {
+    const int st = validate_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    attn::Fp8Args a;
+    a.f = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.q_descale = q_descale;
+    a.k_descale = k_descale;
+    a.v_descale = v_descale;
+    return finish(attn::launch_fwd_fp8(a, stream));
 }
 
 size_t attn_unfused_workspace_bytes(int B, int H, int N, int elem_bytes) {
@@ -149,7 +174,7 @@ size_t attn_unfused_workspace_bytes(int B, int H, int N, int elem_bytes) {
 int attn_fwd_unfused(const void *q, const void *k, const void *v, void *o, float *lse, void *workspace,
                      size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                      hipStream_t stream) {
-    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2);
+    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2, 2);
     if (st < 0) return ATTN_OK;
     if (st != ATTN_OK) return st;
     st = validate_workspace(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, 2);
@@ -164,7 +189,7 @@ int attn_fwd_unfused(const void *q, const void *k, const void *v, void *o, float
 int attn_fwd_unfused_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                          void *workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
                          int causal, hipStream_t stream) {
-    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4);
+    int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 4, 4);
     if (st < 0) return ATTN_OK;
     if (st != ATTN_OK) return st;
     st = validate_workspace(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, 4);
@@ -220,7 +245,7 @@ const char *attn_status_string(int status) {
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_unfused_workspace_bytes()";
         case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
-        case ATTN_ERR_ARG: return "scale must be finite and > 0, causal must be 0 or 1";
+        case ATTN_ERR_ARG: return "scale and fp8 descale factors must be finite and > 0, causal must be 0 or 1";
         default: return "unknown status";
     }
 }

@@ -27,6 +27,16 @@ struct FwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 
+// Fused forward on OCP e4m3 inputs with per-tensor dequantisation factors;
+// f.o is bf16.
+struct Fp8Args {
+    FwdArgs f;
+    float q_descale;
+    float k_descale;
+    float v_descale;
+};
+hipError_t launch_fwd_fp8(const Fp8Args &a, hipStream_t s);
+
 // Unfused forward: scores -> workspace, softmax in place, probabilities x V.
 hipError_t launch_unfused_bf16(const FwdArgs &a, void *ws, hipStream_t s);
 hipError_t launch_unfused_f32(const FwdArgs &a, void *ws, hipStream_t s);

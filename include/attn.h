@@ -55,7 +55,7 @@ typedef enum {
     ATTN_ERR_ALIAS = 5,     /* an output range overlaps an input or another output range   */
     ATTN_ERR_WORKSPACE = 6, /* unfused workspace smaller than attn_unfused_workspace_bytes */
     ATTN_ERR_HIP = 7,       /* a HIP runtime call failed (see attn_last_hip_error)        */
-    ATTN_ERR_ARG = 8        /* scale not finite and > 0, or causal not 0/1                */
+    ATTN_ERR_ARG = 8        /* scale (or an fp8 descale) not finite and > 0, or causal not 0/1 */
 } attn_status;
 
 /*
@@ -81,6 +81,31 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * units, no reduced-precision step).  Same parameters and checks as attn_fwd. */
 int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Fused forward on 8-bit floating-point inputs: the low-precision variant
+ * that "Attention Is Memory-Bound, and Nobody Noticed for Five Years"
+ * reports for the FlashAttention-3 generation (results paragraph), computing
+ * the attn_fwd function of the dequantised inputs
+ *     Q = q_descale * q,   K = k_descale * k,   V = v_descale * v.
+ *   q, k, v : const [B,H,N,d] bytes in the OCP FP8 E4M3 format (1 sign bit,
+ *             4 exponent bits with bias 7, 3 mantissa bits; subnormals; no
+ *             infinities; 0x7F and 0xFF are NaN, which the caller must not
+ *             pass; largest finite value 448)
+ *   o       : bf16 [B,H,N,d] output (real scale, RNE from fp32)
+ *   lse     : float [B,H,N] natural-log log-sum-exp of the real scaled scores
+ *             (scale * Q.K), or NULL
+ *   q_descale, k_descale, v_descale : per-tensor dequantisation factors,
+ *             finite and > 0
+ * Both products run on the fp8 matrix-core instructions with fp32
+ * accumulation; the softmax is fp32; the probabilities are rounded to E4M3
+ * (nearest even, values at most 2^8) before the second product.
+ * Checks: as attn_fwd (alignment 16 bytes for q, k, v and o; per-slice limit
+ * (N+256)*d*2 < 2^32), with the three descale factors checked with scale.
+ */
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int N, int d, float scale,
+                 float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream);
 
 /* Bytes of workspace the unfused variant needs: B*H*N*N*elem_bytes
  * (elem_bytes = 2 for attn_fwd_unfused, 4 for attn_fwd_unfused_f32).  Returns
