@@ -17,7 +17,9 @@ Prints ONE JSON line.  Besides the headline value it carries:
   unfused       -- the three-launch standard path on the same workload, with
                    its algorithmic HBM bytes per second;
   backward      -- attn_bwd (dQ, dK, dV) on the dense 8k and causal 32k
-                   workloads.
+                   workloads;
+  fp8           -- attn_fwd_fp8 (e4m3 Q, K, V, bf16 O) on the dense 8k and
+                   causal 32k shapes, against the fp8 dense MFMA peak.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick]
 """
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused attention fwd TFLOP/s (bf16) + % of MFMA peak, B·H·N²·d sweep"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_FP8_TFLOPS = 5033.2    # twice the bf16 rate (32x32x64 fp8 MFMA)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_attention_124_amd/csrc/attn_fwd_bf16.hip",
                   "exact_attention_124_amd/csrc/common.h"]
@@ -135,6 +138,35 @@ def bench_backward(ea, w, steps, warmup):
     return total_ms, per
 
 
+def bench_fp8(ea, w, steps, warmup):
+    """Time attn_fwd_fp8 on the shape of workload `w` (inputs quantised to e4m3)."""
+    import torch
+    from exact_attention_124_amd.workloads import make_qkv_fp8
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.q_mult, device="cuda")
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: ea.attn_fwd_fp8(q8, k8, v8, o, lse, qd, kd, vd, causal=w.causal, stream=stream)  # noqa
+    total_ms, per = time_launches(call, steps, warmup, stream)
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
+    return total_ms, per
+
+
+def fp8_legs(ea, workloads, steps, warmup):
+    out = []
+    for name in (HEADLINE, "causal_32k_qx8_bf16"):
+        ww = workloads[name]
+        tot, pl = bench_fp8(ea, ww, steps, warmup)
+        fm = sum(pl) / len(pl)
+        tf = ww.flops / (fm * 1e-3) / 1e12
+        out.append({"workload": name.replace("_bf16", "_fp8"), "shape": ww.describe().replace("bf16", "e4m3"),
+                    "ms": round(fm, 4), "TFLOP/s": round(tf, 2),
+                    "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
+        log(f"[bench] fp8 {name}: {fm:.4f} ms, {out[-1]['TFLOP/s']} TFLOP/s")
+    return out
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device copy of known size (for scaling the byte counters)."""
     import torch
@@ -204,6 +236,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only the fp8 forward legs (for kernel traces of that kernel)")
     ap.add_argument("--n-sweep", action="store_true",
                     help="only run fused and unfused once each at B=1 H=32 d=128 for N = 1k..16k "
                          "(for HBM byte counters), plus the copy calibration")
@@ -225,6 +259,9 @@ def main():
 
     if args.n_sweep:
         n_sweep(ea)
+        return
+    if args.fp8_only:
+        print(json.dumps({"fp8": fp8_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
         return
 
     w = WORKLOADS[HEADLINE]
@@ -306,6 +343,7 @@ def main():
                                            "14*B*H*N^2*d (S and dP are recomputed for dQ)"})
             log(f"[bench] backward {name}: {bm:.3f} ms, {bwd[-1]['TFLOP/s']} TFLOP/s")
         result["backward"] = bwd
+        result["fp8"] = fp8_legs(ea, WORKLOADS, 10, 3)
 
         if not args.no_cpu:
             log("[bench] timing the CPU oracle on a bounded sample")

@@ -25,8 +25,9 @@
 //    of one head dim to every lane.  The key order of the four reads matches
 //    the order in which the score accumulator holds its keys.
 //  * O = v_descale * acc / l, stored as bf16; lse as in the bf16 kernel.
-// Tiles, pipelining (K one tile ahead of V), causal skipping, the heaviest-
-// first order of causal query blocks and the XCD remap follow the bf16 kernel.
+// Tiles are 128 keys, double-buffered in LDS (32 KiB per K or V tile pair at
+// d = 128); causal skipping, the heaviest-first order of causal query blocks
+// and the XCD remap follow the bf16 kernel.
 #include "common.h"
 #include "launch.h"
 
@@ -53,8 +54,11 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t *p) {
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 // Four floats -> four e4m3 bytes (round to nearest even), a in the low byte.
-__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// The two conversions overwrite both 16-bit halves of `dst`, the register
+// the packed word is stored in (its old contents are dead), so no zeroed or
+// copied destination has to be materialised.
+__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d, int dst) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, dst, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -127,7 +131,7 @@ struct Layout {
 
 constexpr float kLazyThreshold = 8.0f;  // log2 units; probabilities stay <= 2^8 < 448
 
-template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
+template <int D, bool CAUSAL, int WAVES, int BC>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kernel(Params p) {
     using T = Tile<D, WAVES, BC>;
@@ -255,7 +259,7 @@ void kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
         }
-        float rs0 = 0.f, rs1 = 0.f;
+        float rs0, rs1;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -264,9 +268,15 @@ void kernel(Params p) {
                 const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
                 const float p2 = fast_exp2(fmaf(s[b][r + 2], c, -m_run));
                 const float p3 = fast_exp2(fmaf(s[b][r + 3], c, -m_run));
-                rs0 += p0 + p2;
-                rs1 += p1 + p3;
-                pf[b >> 1][4 * (b & 1) + (r >> 2)] = pack_e4m3x4(p0, p1, p2, p3);
+                if (b == 0 && r == 0) {
+                    rs0 = p0 + p2;
+                    rs1 = p1 + p3;
+                } else {
+                    rs0 += p0 + p2;
+                    rs1 += p1 + p3;
+                }
+                const int slot = 4 * (b & 1) + (r >> 2);
+                pf[b >> 1][slot] = pack_e4m3x4(p0, p1, p2, p3, pf[b >> 1][slot]);
             }
         }
         l_run += rs0 + rs1;
@@ -286,55 +296,28 @@ void kernel(Params p) {
         }
     };
 
-    if constexpr (KAHEAD) {
-        load_k(0, 0);
-        load_v(0, 0);
-        if (ntiles > 1) load_k(1, 1);
+    i32x8 pf[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) pf[g] = i32x8{};
+    // Double-buffered tiles: tile j+1 streams into LDS while tile j is used.
+    load_k(0, 0);
+    load_v(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles) {
+            load_k(j + 1, buf ^ 1);
+            load_v(j + 1, buf ^ 1);
+        }
+        if (active(j)) {
+            f32x16 s[NB];
+            scores(buf, s);
+            softmax(j, s, pf, j >= nfull);
+            pv(buf, pf);
+        }
         wait_vmem();
         __syncthreads();
-        f32x16 sa[NB], sb[NB];
-        if (active(0)) scores(0, sa);
-        auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
-            if (j + 2 < ntiles) load_k(j + 2, j & 1);
-            if (j + 1 < ntiles) {
-                load_v(j + 1, (j + 1) & 1);
-                if (active(j + 1)) scores((j + 1) & 1, nxt);
-            }
-            if (active(j)) {
-                i32x8 pf[NG];
-                softmax(j, cur, pf, j >= nfull);
-                pv(j & 1, pf);
-            }
-            wait_vmem();
-            __syncthreads();
-        };
-        int j = 0;
-        for (; j + 1 < ntiles; j += 2) {
-            step(j, sa, sb);
-            step(j + 1, sb, sa);
-        }
-        if (j < ntiles) step(j, sa, sb);
-    } else {
-        load_k(0, 0);
-        load_v(0, 0);
-        wait_vmem();
-        __syncthreads();
-        for (int j = 0; j < ntiles; ++j) {
-            const int buf = j & 1;
-            if (j + 1 < ntiles) {
-                load_k(j + 1, buf ^ 1);
-                load_v(j + 1, buf ^ 1);
-            }
-            if (active(j)) {
-                f32x16 s[NB];
-                i32x8 pf[NG];
-                scores(buf, s);
-                softmax(j, s, pf, j >= nfull);
-                pv(buf, pf);
-            }
-            wait_vmem();
-            __syncthreads();
-        }
     }
 
     const float l_tot = pair_sum(l_run);
@@ -354,7 +337,7 @@ void kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
+template <int D, bool CAUSAL, int WAVES, int BC>
 hipError_t launch(const Fp8Args &a, hipStream_t s) {
     using T = Tile<D, WAVES, BC>;
     Params p;
@@ -368,21 +351,23 @@ hipError_t launch(const Fp8Args &a, hipStream_t s) {
     p.scale_log2 = a.f.scale * a.q_descale * a.k_descale * kLog2e;
     p.v_descale = a.v_descale;
     const unsigned blocks = (unsigned)a.f.BH * (unsigned)p.nqb;
-    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
+    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace fwd_fp8
 
 #ifndef ATTN_FWD_FP8_NO_DEFAULT_LAUNCHER
-// Same workgroup-shape policy as the bf16 kernel: 8 waves with the K-ahead
-// pipeline when that still gives four workgroups per CU, else 4 waves.
+// 128-key tiles.  8 waves (256 query rows) per workgroup for dense grids of
+// at least four such workgroups per CU, else 4 waves (128 rows, two
+// workgroups per CU); causal sequences always take 4 waves, whose shorter
+// blocks waste less work on the diagonal.
 template <int D, bool CAUSAL>
 static hipError_t launch_fp8_d(const Fp8Args &a, hipStream_t s) {
     using namespace fwd_fp8;
     const long long blocks8 = (long long)a.f.BH * ((a.f.N + 255) / 256);
-    const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.f.N <= 4096);
-    return wide ? launch<D, CAUSAL, 8, 64, true>(a, s) : launch<D, CAUSAL, 4, 64, false>(a, s);
+    const bool wide = !CAUSAL && blocks8 >= 4 * 256;
+    return wide ? launch<D, CAUSAL, 8, 128>(a, s) : launch<D, CAUSAL, 4, 128>(a, s);
 }
 
 hipError_t launch_fwd_fp8(const Fp8Args &a, hipStream_t s) {
