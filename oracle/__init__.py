@@ -25,7 +25,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "attn_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c"),
-         os.path.join(_HERE, "attn_probs_oracle.c")]
+         os.path.join(_HERE, "attn_probs_oracle.c"), os.path.join(_HERE, "attn_masked_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
@@ -78,6 +78,15 @@ def _load():
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,      # S N d
         ctypes.c_double, ctypes.c_int,                       # scale causal
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,       # rows n_rows threads
+    ]
+    lib.oracle_attn_masked_f64.restype = ctypes.c_int
+    lib.oracle_attn_masked_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,   # q k v bias
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,                      # sb sh si
+        ctypes.c_void_p, ctypes.c_void_p,                                    # o lse
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,      # B H N d
+        ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,       # scale causal wl wr
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,                       # rows n_rows threads
     ]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
@@ -191,6 +200,42 @@ def attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: flo
     qd, kd, vd = (float(np.float32(x)) for x in (q_descale, k_descale, v_descale))
     return attention(decode_e4m3(q8) * qd, decode_e4m3(k8) * kd, decode_e4m3(v8) * vd, scale, causal,
                      rows=rows, threads=threads)
+
+
+def attention_masked(q, k, v, scale: float, causal: bool = False, window_left: int = -1,
+                     window_right: int = -1, bias=None, rows=None, threads: int = 0):
+    """Exact attention with a causal / sliding-window mask and an additive
+    bias, fp64.  ``q``, ``k``, ``v``: ``[B, H, N, d]``.  ``bias``: None, or an
+    array broadcastable to ``[B, H, N, N]`` (added to the scaled scores; -inf
+    removes a key).  A window side < 0 is unbounded.  Rows with no allowed
+    finite score give o = 0 and lse = -inf.  Returns ``(o, lse)`` shaped
+    ``[B, H, R, d]`` and ``[B, H, R]``."""
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    if not (q64.shape == k64.shape == v64.shape) or q64.ndim != 4:
+        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    B, H, N, d = q64.shape
+    if bias is not None:
+        b64 = _as_f64(bias)
+        if b64.ndim != 4 or b64.shape[2:] != (N, N) or b64.shape[0] not in (1, B) or b64.shape[1] not in (1, H):
+            raise ValueError("bias must be [B|1, H|1, N, N]")
+        b64 = np.ascontiguousarray(b64)
+        sb = 0 if b64.shape[0] == 1 else b64.shape[1] * N * N
+        sh = 0 if b64.shape[1] == 1 else N * N
+        si = N
+    else:
+        b64, sb, sh, si = None, 0, 0, 0
+    r = _index(rows)
+    R = N if r is None else r.size
+    o = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    rc = _load().oracle_attn_masked_f64(
+        q64.ctypes.data, k64.ctypes.data, v64.ctypes.data, b64.ctypes.data if b64 is not None else None,
+        sb, sh, si, o.ctypes.data, lse.ctypes.data, B, H, N, d, float(scale), 1 if causal else 0,
+        int(window_left), int(window_right), r.ctypes.data if r is not None else None,
+        R if r is not None else 0, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_masked_f64 failed with code {rc}")
+    return o, lse
 
 
 def _index(idx):
