@@ -19,6 +19,7 @@ __all__ = [
     "attn_fwd_unfused_f32", "attn_unfused_workspace_bytes", "attn_status_string",
     "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
     "attn_bwd_workspace_bytes", "attention_backward", "attn_fwd_fp8", "attention_fp8",
+    "attn_fwd_masked", "attention_masked",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +64,9 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = I
+    LL = ctypes.c_longlong
+    lib.attn_fwd_masked.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, I, P, LL, LL, LL, P]
+    lib.attn_fwd_masked.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P]
     lib.attn_fwd_fp8.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
@@ -209,6 +213,40 @@ def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False,
         raise AttnError(st, "attn_fwd_fp8")
 
 
+def _bias_view(bias, B, H, N, device):
+    """(pointer, stride_b, stride_h, stride_i) of a float32 bias broadcastable
+    to [B, H, N, N]: shape [N, N] or [B|1, H|1, N, N], last stride 1."""
+    torch = _torch()
+    if bias is None:
+        return None, 0, 0, 0
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.device != device:
+        raise TypeError("bias must be a float32 tensor on q's device")
+    if bias.dim() == 2:
+        bias = bias.unsqueeze(0).unsqueeze(0)
+    if bias.dim() != 4 or tuple(bias.shape[2:]) != (N, N) or bias.shape[0] not in (1, B) \
+            or bias.shape[1] not in (1, H) or bias.stride(3) != 1:
+        raise ValueError("bias must be [N, N] or [B|1, H|1, N, N] with unit stride along keys")
+    sb = 0 if bias.shape[0] == 1 else bias.stride(0)
+    sh = 0 if bias.shape[1] == 1 else bias.stride(1)
+    return bias.data_ptr(), sb, sh, bias.stride(2)
+
+
+def attn_fwd_masked(q, k, v, o, lse=None, causal=False, window=(-1, -1), bias=None, scale=None, stream=None):
+    """bf16 fused forward with a causal / sliding-window mask and an optional
+    float32 additive bias, into caller-allocated ``o`` (and ``lse``).
+    ``window`` = (left, right); a negative side is unbounded."""
+    torch = _torch()
+    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
+    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
+    bp, sb, sh, si = _bias_view(bias, B, H, N, q.device)
+    wl, wr = (int(window[0]), int(window[1]))
+    st = load_library().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                                        B, H, N, d, _scale(scale, d), 1 if causal else 0, wl, wr, bp, sb, sh, si,
+                                        _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_masked")
+
+
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
     """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv``."""
     torch = _torch()
@@ -254,6 +292,15 @@ def attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal, scale, stream)
+    return o, lse
+
+
+def attention_masked(q, k, v, causal=False, window=(-1, -1), bias=None, scale=None, stream=None):
+    """Masked / biased fused forward; returns ``(o, lse)``."""
+    torch = _torch()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_masked(q, k, v, o, lse, causal, window, bias, scale, stream)
     return o, lse
 
 

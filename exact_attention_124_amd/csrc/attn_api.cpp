@@ -105,6 +105,26 @@ int validate_fp8(const void *q, const void *k, const void *v, const void *o, con
     return validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 1, 2);
 }
 
+// Masked forward: bf16 tensors as attn_fwd; the bias must be 4-byte aligned
+// with non-negative strides, its per-wave row offsets must fit 32 bits, and
+// it must not overlap o or lse.
+int validate_masked(const void *q, const void *k, const void *v, const void *o, const float *lse, int B, int H,
+                    int N, int d, float scale, int causal, const float *bias, long long sb, long long sh,
+                    long long si) {
+    const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2, 2);
+    if (st != ATTN_OK || !bias) return st;
+    if (sb < 0 || sh < 0 || si < 0) return ATTN_ERR_ARG;
+    if (!aligned(bias, 4)) return ATTN_ERR_ALIGN;
+    if ((32.0 * (double)si + N + 64) * 4.0 >= 4294967296.0) return ATTN_ERR_SHAPE;
+    const double ext = (double)(B - 1) * sb + (double)(H - 1) * sh + (double)(N - 1) * si + N;
+    if (ext * 4.0 >= 9.0e18) return ATTN_ERR_SHAPE;
+    const Range rb = range_of(bias, (size_t)ext * 4);
+    const size_t elems = (size_t)B * H * (size_t)N * d;
+    if (overlaps(rb, range_of(o, elems * 2))) return ATTN_ERR_ALIAS;
+    if (lse && overlaps(rb, range_of(lse, (size_t)B * H * (size_t)N * sizeof(float)))) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
 int validate_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                  const void *dq, const void *dk, const void *dv, const void *ws, size_t ws_bytes, int B, int H,
                  int N, int d, float scale, int causal) {
@@ -161,6 +181,26 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *ls
     a.k_descale = k_descale;
     a.v_descale = v_descale;
     return finish(attn::launch_fwd_fp8(a, stream));
+}
+
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+                    float scale, int causal, int window_left, int window_right, const float *bias,
+                    long long bias_stride_b, long long bias_stride_h, long long bias_stride_i,
+                    hipStream_t stream) {
+    const int st = validate_masked(q, k, v, o, lse, B, H, N, d, scale, causal, bias, bias_stride_b, bias_stride_h,
+                                   bias_stride_i);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    attn::MaskedArgs a;
+    a.f = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.H = H;
+    a.window_left = window_left < 0 ? -1 : window_left;
+    a.window_right = window_right < 0 ? -1 : window_right;
+    a.bias = bias;
+    a.bias_stride_b = bias_stride_b;
+    a.bias_stride_h = bias_stride_h;
+    a.bias_stride_i = bias_stride_i;
+    return finish(attn::launch_fwd_masked(a, stream));
 }
 
 size_t attn_unfused_workspace_bytes(int B, int H, int N, int elem_bytes) {

@@ -37,6 +37,20 @@ struct Fp8Args {
 };
 hipError_t launch_fwd_fp8(const Fp8Args &a, hipStream_t s);
 
+// Fused forward with a causal / sliding-window mask and an optional fp32
+// additive bias (element (b, h, i, j) at bias + b*sb + h*sh + i*si + j).
+struct MaskedArgs {
+    FwdArgs f;
+    int H;
+    int window_left;   // < 0: unbounded
+    int window_right;  // < 0: unbounded
+    const float *bias;
+    long long bias_stride_b;
+    long long bias_stride_h;
+    long long bias_stride_i;
+};
+hipError_t launch_fwd_masked(const MaskedArgs &a, hipStream_t s);
+
 // Unfused forward: scores -> workspace, softmax in place, probabilities x V.
 hipError_t launch_unfused_bf16(const FwdArgs &a, void *ws, hipStream_t s);
 hipError_t launch_unfused_f32(const FwdArgs &a, void *ws, hipStream_t s);

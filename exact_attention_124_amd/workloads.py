@@ -17,6 +17,10 @@ head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
   generator seeded with ``seed + 1``;
 * the upstream gradient dO of the backward: float32 ``randn`` of the same
   shape from a generator seeded with ``seed + 100``, then the working dtype;
+* additive attention bias: float32 ``randn`` of shape ``[Bb, Hb, N, N]`` from
+  a generator seeded with ``seed + 200``, times ``scale``, with a fraction
+  ``drop`` of entries (never a diagonal one) set to -inf, chosen by a second
+  generator seeded with ``seed + 201``;
 * 8-bit inputs: the float32 ``Q``, ``K``, ``V`` above, each divided by its
   per-tensor factor ``descale = max|x| / 448`` (float32) and converted to
   ``torch.float8_e4m3fn`` (round to nearest even; the largest magnitude lands
@@ -93,6 +97,18 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype=torch.bfloat16, seed: int = 0
         t = t.to(dtype)
         out.append(t.to(device) if str(device) != "cpu" else t)
     return tuple(out)
+
+
+def make_bias(Bb: int, Hb: int, N: int, seed: int = 0, scale: float = 1.0, drop: float = 0.0, device="cpu"):
+    """Additive bias [Bb, Hb, N, N] (see the module docstring)."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 200)
+    b = torch.randn((Bb, Hb, N, N), generator=g, dtype=torch.float32) * scale
+    if drop > 0:
+        g2 = torch.Generator(device="cpu").manual_seed(seed + 201)
+        m = torch.rand((Bb, Hb, N, N), generator=g2) < drop
+        m &= ~torch.eye(N, dtype=torch.bool)
+        b.masked_fill_(m, float("-inf"))
+    return b.to(device) if str(device) != "cpu" else b
 
 
 E4M3_MAX = 448.0

@@ -107,6 +107,37 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *ls
                  int B, int H, int N, int d, float scale,
                  float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream);
 
+/*
+ * Fused forward with a general mask and an additive bias, bfloat16: the
+ * custom masks and attention biases that the pages name as what usually
+ * takes attention off the fused path ("Attention Is Memory-Bound, and Nobody
+ * Noticed for Five Years", the paragraph on what the result means in
+ * practice), computed on it:
+ *     s[b,h,i,j] = scale * q[b,h,i,:] . k[b,h,j,:] + bias[b,h,i,j]
+ * over the keys j allowed for query i, softmax over them, times v.
+ *   causal        : 0/1, as attn_fwd
+ *   window_left   : key j allowed only if j >= i - window_left (< 0: no limit)
+ *   window_right  : key j allowed only if j <= i + window_right (< 0: no limit)
+ *   bias          : NULL, or float32 with element (b,h,i,j) at
+ *                   bias[b*bias_stride_b + h*bias_stride_h + i*bias_stride_i + j]
+ *                   (strides in elements, >= 0; 0 broadcasts over that
+ *                   index); -inf removes a key (a boolean mask).  A bias
+ *                   16-byte aligned with strides that are multiples of 4 is
+ *                   read 16 bytes at a time, any other 4 bytes at a time
+ * A query row with no allowed key of finite score gets o = 0 and lse = -inf.
+ * Key tiles outside a workgroup's allowed range are skipped, so a sliding
+ * window costs work proportional to its width.
+ * Checks: as attn_fwd, then (bias only) strides >= 0 (ATTN_ERR_ARG), bias
+ * 4-byte aligned (ATTN_ERR_ALIGN),
+ * (32*bias_stride_i + N + 64)*4 < 2^32 (ATTN_ERR_SHAPE), and the bias extent
+ * not overlapping o or lse (ATTN_ERR_ALIAS).
+ */
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    int window_left, int window_right, const float *bias,
+                    long long bias_stride_b, long long bias_stride_h, long long bias_stride_i,
+                    hipStream_t stream);
+
 /* Bytes of workspace the unfused variant needs: B*H*N*N*elem_bytes
  * (elem_bytes = 2 for attn_fwd_unfused, 4 for attn_fwd_unfused_f32).  Returns
  * 0 for non-positive arguments or on size_t overflow.  Pure host function. */

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_unfused", "attn_fwd_unfused_f32",
                             "attn_unfused_workspace_bytes", "attn_status_string",
-                            "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8"])
+                            "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_fwd_masked"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -162,6 +162,29 @@ def test_fp8_validation_codes(lib):
     assert fp8(lib, o=V - 65536 + 16) == S["ATTN_ERR_ALIAS"]   # o's tail runs into v
     assert fp8(lib, lse=O + 65536 - 4) == S["ATTN_ERR_ALIAS"]  # lse starts inside o
     assert fp8(lib, N=1 << 26, d=128) == S["ATTN_ERR_SHAPE"]   # 32-bit slice offsets of o
+
+
+BIAS = A + 10 * GAP
+
+
+def masked(lib, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=256, d=64, scale=0.125, causal=0, wl=-1, wr=-1,
+           bias=BIAS, sb=0, sh=256 * 256, si=256):
+    return lib.attn_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, causal, wl, wr, bias, sb, sh, si, None)
+
+
+def test_masked_validation_codes(lib):
+    S = __import__("exact_attention_124_amd").STATUS
+    # Every call below fails validation or is empty: nothing is launched.
+    assert masked(lib, q=None) == S["ATTN_ERR_NULL"]
+    assert masked(lib, N=0) == S["ATTN_OK"]
+    assert masked(lib, d=80) == S["ATTN_ERR_HEAD_DIM"]
+    assert masked(lib, causal=5) == S["ATTN_ERR_ARG"]
+    assert masked(lib, sb=-4) == S["ATTN_ERR_ARG"]
+    assert masked(lib, bias=BIAS + 2) == S["ATTN_ERR_ALIGN"]
+    assert masked(lib, si=1 << 25) == S["ATTN_ERR_SHAPE"]          # 32-bit row offsets
+    assert masked(lib, bias=O + 1024) == S["ATTN_ERR_ALIAS"]        # bias inside o
+    assert masked(lib, bias=L - 16, sh=0, si=0) == S["ATTN_ERR_ALIAS"]  # [N] row runs into lse
+    assert masked(lib, o=Q) == S["ATTN_ERR_ALIAS"]
 
 
 DO, DQ, DK, DV = (A + i * GAP for i in range(6, 10))
