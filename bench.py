@@ -19,7 +19,10 @@ Prints ONE JSON line.  Besides the headline value it carries:
   backward      -- attn_bwd (dQ, dK, dV) on the dense 8k and causal 32k
                    workloads;
   fp8           -- attn_fwd_fp8 (e4m3 Q, K, V, bf16 O) on the dense 8k and
-                   causal 32k shapes, against the fp8 dense MFMA peak.
+                   causal 32k shapes, against the fp8 dense MFMA peak;
+  masked        -- attn_fwd_masked: dense 8k with an [N, N] fp32 bias, and
+                   causal 32k with a 4096-key sliding window (FLOPs counted
+                   over allowed (query, key) pairs only).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick]
 """
@@ -167,6 +170,42 @@ def fp8_legs(ea, workloads, steps, warmup):
     return out
 
 
+def masked_legs(ea, workloads, steps, warmup):
+    import torch
+    from exact_attention_124_amd.workloads import make_bias, workload_inputs
+    out = []
+    stream = torch.cuda.current_stream()
+    for name, window, with_bias in ((HEADLINE, (-1, -1), True), ("causal_32k_qx8_bf16", (4096, -1), False)):
+        w = workloads[name]
+        q, k, v = workload_inputs(w, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        bias = make_bias(1, 1, w.N, seed=w.seed, device="cuda").expand(w.B, w.H, w.N, w.N) if with_bias else None
+        call = lambda: ea.attn_fwd_masked(q, k, v, o, lse, causal=w.causal, window=window, bias=bias,  # noqa
+                                          stream=stream)
+        tot, pl = time_launches(call, steps, warmup, stream)
+        ms = sum(pl) / len(pl)
+        wl = window[0]
+        if w.causal and wl >= 0:
+            pairs = sum(min(i, wl) + 1 for i in range(w.N))
+        elif w.causal:
+            pairs = w.N * (w.N + 1) // 2
+        else:
+            pairs = w.N * w.N
+        fl = 4.0 * w.B * w.H * pairs * w.d
+        rec = {"workload": name, "window": list(window), "bias": "[N,N] fp32" if with_bias else None,
+               "ms": round(ms, 4), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+               "flop_convention": "4*B*H*d per allowed (query, key) pair"}
+        if with_bias:
+            rec["bias_bytes_read"] = w.B * w.H * w.N * w.N * 4
+            rec["bias_GB/s"] = round(rec["bias_bytes_read"] / (ms * 1e-3) / 1e9, 1)
+        out.append(rec)
+        log(f"[bench] masked {name} window={window} bias={with_bias}: {ms:.4f} ms, {rec['TFLOP/s']} TFLOP/s")
+        del q, k, v, o, lse, bias
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device copy of known size (for scaling the byte counters)."""
     import torch
@@ -236,6 +275,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--masked-only", action="store_true",
+                    help="only the masked / biased forward legs")
     ap.add_argument("--fp8-only", action="store_true",
                     help="only the fp8 forward legs (for kernel traces of that kernel)")
     ap.add_argument("--n-sweep", action="store_true",
@@ -259,6 +300,9 @@ def main():
 
     if args.n_sweep:
         n_sweep(ea)
+        return
+    if args.masked_only:
+        print(json.dumps({"masked": masked_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
         return
     if args.fp8_only:
         print(json.dumps({"fp8": fp8_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
@@ -344,6 +388,7 @@ def main():
             log(f"[bench] backward {name}: {bm:.3f} ms, {bwd[-1]['TFLOP/s']} TFLOP/s")
         result["backward"] = bwd
         result["fp8"] = fp8_legs(ea, WORKLOADS, 10, 3)
+        result["masked"] = masked_legs(ea, WORKLOADS, 10, 3)
 
         if not args.no_cpu:
             log("[bench] timing the CPU oracle on a bounded sample")
