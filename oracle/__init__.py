@@ -238,6 +238,26 @@ def attention_masked(q, k, v, scale: float, causal: bool = False, window_left: i
     return o, lse
 
 
+# ---------------------------------------------------------------------------
+# Elementwise chain (the fusion example of the pages).
+# ---------------------------------------------------------------------------
+def elementwise_chain(x, scale: float, bias):
+    """y = relu(scale * x + bias) in fp64, element by element, for a
+    ``[rows, cols]`` array ``x`` and a ``[cols]`` bias broadcast over rows:
+    multiply by a scalar, add a bias, apply an activation ("Attention Is
+    Memory-Bound, and Nobody Noticed for Five Years", the elementwise-chain
+    paragraph; ReLU is the reading of "an activation").  Also returns the two
+    intermediate tensors ``(t1, t2)`` = (scale * x, t1 + bias)."""
+    x64 = _as_f64(x)
+    b64 = _as_f64(bias)
+    if x64.ndim != 2 or b64.shape != (x64.shape[1],):
+        raise ValueError("x must be [rows, cols] and bias [cols]")
+    t1 = float(np.float32(scale)) * x64
+    t2 = t1 + b64[None, :]
+    y = np.where(t2 > 0.0, t2, 0.0)
+    return y, t1, t2
+
+
 def _index(idx):
     if idx is None:
         return None
