@@ -19,7 +19,7 @@ __all__ = [
     "attn_fwd_unfused_f32", "attn_unfused_workspace_bytes", "attn_status_string",
     "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
     "attn_bwd_workspace_bytes", "attention_backward", "attn_fwd_fp8", "attention_fp8",
-    "attn_fwd_masked", "attention_masked",
+    "attn_fwd_masked", "attention_masked", "ew_chain_fused", "ew_chain_unfused", "elementwise_chain",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,10 @@ def load_library() -> ctypes.CDLL:
     LL = ctypes.c_longlong
     lib.attn_fwd_masked.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, I, P, LL, LL, LL, P]
     lib.attn_fwd_masked.restype = I
+    for name in ("ew_chain_fused", "ew_chain_unfused"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, P, P, LL, I, F, P]
+        fn.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P]
     lib.attn_fwd_fp8.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
@@ -245,6 +249,40 @@ def attn_fwd_masked(q, k, v, o, lse=None, causal=False, window=(-1, -1), bias=No
                                         _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, "attn_fwd_masked")
+
+
+def _ew(name, x, y, bias, scale, stream):
+    torch = _torch()
+    for nm, t in (("x", x), ("y", y)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() \
+                or t.device.type != "cuda":
+            raise ValueError(f"{nm} must be a contiguous bf16 [rows, cols] tensor on a GPU")
+    if tuple(y.shape) != tuple(x.shape) or y.device != x.device:
+        raise ValueError("y must have x's shape and device")
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or tuple(bias.shape) != (x.shape[1],) \
+            or not bias.is_contiguous() or bias.device != x.device:
+        raise ValueError("bias must be a contiguous float32 [cols] tensor on x's device")
+    st = getattr(load_library(), name)(x.data_ptr(), y.data_ptr(), bias.data_ptr(), x.shape[0], x.shape[1],
+                                       float(scale), _stream(stream, x.device))
+    if st != 0:
+        raise AttnError(st, name)
+
+
+def ew_chain_fused(x, y, bias, scale, stream=None):
+    """y = relu(scale * x + bias) in one launch (bf16 x, y; float32 bias)."""
+    _ew("ew_chain_fused", x, y, bias, scale, stream)
+
+
+def ew_chain_unfused(x, y, bias, scale, stream=None):
+    """The same chain as three launches, each reading and writing the tensor."""
+    _ew("ew_chain_unfused", x, y, bias, scale, stream)
+
+
+def elementwise_chain(x, bias, scale, fused=True, stream=None):
+    """Allocating form of ew_chain_fused / ew_chain_unfused."""
+    y = _torch().empty_like(x)
+    (ew_chain_fused if fused else ew_chain_unfused)(x, y, bias, scale, stream)
+    return y
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_unfused.hip", "attn_bwd_bf16.hip",
-           "attn_fwd_fp8.hip", "attn_fwd_masked.hip"]
+           "attn_fwd_fp8.hip", "attn_fwd_masked.hip", "ew_chain.hip"]
 # Per-file extra flags.  The fused bf16 kernel never produces or relies on NaN
 # (inputs are required to be finite), which lets max reductions use v_max3
 # without canonicalising every operand.

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "../../include/attn.h"
+#include "../../include/ew_chain.h"
 #include "launch.h"
 
 namespace {
@@ -122,6 +123,21 @@ int validate_masked(const void *q, const void *k, const void *v, const void *o, 
     const size_t elems = (size_t)B * H * (size_t)N * d;
     if (overlaps(rb, range_of(o, elems * 2))) return ATTN_ERR_ALIAS;
     if (lse && overlaps(rb, range_of(lse, (size_t)B * H * (size_t)N * sizeof(float)))) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+int validate_ew(const void *x, const void *y, const float *bias, long long rows, int cols, float scale) {
+    if (rows < 0 || cols < 0) return ATTN_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return -1;
+    if (!x || !y || !bias) return ATTN_ERR_NULL;
+    if (cols % 8) return ATTN_ERR_SHAPE;
+    if (!isfinite(scale)) return ATTN_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(bias, 16)) return ATTN_ERR_ALIGN;
+    if ((unsigned __int128)rows * (unsigned)cols * 2u >= ((unsigned __int128)1 << 62)) return ATTN_ERR_SHAPE;
+    const size_t bytes = (size_t)rows * (size_t)cols * 2;
+    const Range rx = range_of(x, bytes), ry = range_of(y, bytes), rb = range_of(bias, (size_t)cols * 4);
+    if (x != y && overlaps(rx, ry)) return ATTN_ERR_ALIAS;  // in place is allowed, partial overlap is not
+    if (overlaps(rb, ry)) return ATTN_ERR_ALIAS;
     return ATTN_OK;
 }
 
@@ -273,6 +289,22 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     a.scale = scale;
     a.causal = causal;
     return finish(attn::launch_bwd_bf16(a, stream));
+}
+
+int ew_chain_fused(const void *x, void *y, const float *bias, long long rows, int cols, float scale,
+                   hipStream_t stream) {
+    const int st = validate_ew(x, y, bias, rows, cols, scale);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    return finish(attn::launch_ew_fused(attn::EwArgs{x, y, bias, rows, cols, scale}, stream));
+}
+
+int ew_chain_unfused(const void *x, void *y, const float *bias, long long rows, int cols, float scale,
+                     hipStream_t stream) {
+    const int st = validate_ew(x, y, bias, rows, cols, scale);
+    if (st < 0) return ATTN_OK;
+    if (st != ATTN_OK) return st;
+    return finish(attn::launch_ew_unfused(attn::EwArgs{x, y, bias, rows, cols, scale}, stream));
 }
 
 const char *attn_status_string(int status) {

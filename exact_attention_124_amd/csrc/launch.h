@@ -76,6 +76,19 @@ struct BwdArgs {
 // Backward: row statistics, then dK/dV, then dQ (three launches).
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
 
+// Elementwise chain y = relu(scale * x + bias) over a [rows, cols] bf16
+// tensor (cols a multiple of 8), fused (one launch) or as three launches.
+struct EwArgs {
+    const void *x;
+    void *y;
+    const float *bias;  // [cols]
+    long long rows;
+    int cols;
+    float scale;
+};
+hipError_t launch_ew_fused(const EwArgs &e, hipStream_t s);
+hipError_t launch_ew_unfused(const EwArgs &e, hipStream_t s);
+
 // Query-row block of the fused bf16 kernel (used for grid-size limits).
 constexpr int kFwdBlockRows = 128;
 

@@ -21,6 +21,9 @@ head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
   a generator seeded with ``seed + 200``, times ``scale``, with a fraction
   ``drop`` of entries (never a diagonal one) set to -inf, chosen by a second
   generator seeded with ``seed + 201``;
+* elementwise chain: x float32 ``randn`` ``[rows, cols]`` rounded to bf16
+  and a float32 ``randn`` bias ``[cols]``, from a generator seeded with
+  ``seed + 300`` (x first);
 * 8-bit inputs: the float32 ``Q``, ``K``, ``V`` above, each divided by its
   per-tensor factor ``descale = max|x| / 448`` (float32) and converted to
   ``torch.float8_e4m3fn`` (round to nearest even; the largest magnitude lands
@@ -109,6 +112,16 @@ def make_bias(Bb: int, Hb: int, N: int, seed: int = 0, scale: float = 1.0, drop:
         m &= ~torch.eye(N, dtype=torch.bool)
         b.masked_fill_(m, float("-inf"))
     return b.to(device) if str(device) != "cpu" else b
+
+
+def make_chain(rows: int, cols: int, seed: int = 0, device="cpu"):
+    """x (bf16 [rows, cols]) and bias (float32 [cols]) of the elementwise chain."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 300)
+    x = torch.randn((rows, cols), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((cols,), generator=g, dtype=torch.float32)
+    if str(device) != "cpu":
+        x, b = x.to(device), b.to(device)
+    return x, b
 
 
 E4M3_MAX = 448.0

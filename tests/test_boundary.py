@@ -9,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+EW_HEADER = os.path.join(ROOT, "include", "ew_chain.h")
 
 
 @pytest.fixture(scope="module")
@@ -20,10 +21,10 @@ def lib():
     return ea.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER, prefix="attn_"):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -33,8 +34,12 @@ def test_header_declares_the_boundary():
                             "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_fwd_masked"])
 
 
+def test_ew_header_declares_the_chain():
+    assert declared_functions(EW_HEADER, "ew_") == ["ew_chain_fused", "ew_chain_unfused"]
+
+
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(EW_HEADER, "ew_"):
         assert hasattr(lib, name), name
         ctypes.cast(getattr(lib, name), ctypes.c_void_p)
 
@@ -185,6 +190,29 @@ def test_masked_validation_codes(lib):
     assert masked(lib, bias=O + 1024) == S["ATTN_ERR_ALIAS"]        # bias inside o
     assert masked(lib, bias=L - 16, sh=0, si=0) == S["ATTN_ERR_ALIAS"]  # [N] row runs into lse
     assert masked(lib, o=Q) == S["ATTN_ERR_ALIAS"]
+
+
+def ew(lib, name, x=Q, y=O, bias=BIAS, rows=64, cols=768, scale=0.5):
+    getattr(lib, name).argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_longlong, ctypes.c_int, ctypes.c_float,
+                                                            ctypes.c_void_p]
+    return getattr(lib, name)(x, y, bias, rows, cols, scale, None)
+
+
+@pytest.mark.parametrize("name", ["ew_chain_fused", "ew_chain_unfused"])
+def test_ew_validation_codes(lib, name):
+    S = __import__("exact_attention_124_amd").STATUS
+    # Every call below fails validation or is empty: nothing is launched.
+    assert ew(lib, name, rows=0) == S["ATTN_OK"]
+    assert ew(lib, name, cols=0, x=None) == S["ATTN_OK"]
+    assert ew(lib, name, rows=-1) == S["ATTN_ERR_SHAPE"]
+    assert ew(lib, name, x=None) == S["ATTN_ERR_NULL"]
+    assert ew(lib, name, bias=None) == S["ATTN_ERR_NULL"]
+    assert ew(lib, name, cols=770) == S["ATTN_ERR_SHAPE"]
+    assert ew(lib, name, scale=float("nan")) == S["ATTN_ERR_ARG"]
+    assert ew(lib, name, y=O + 8) == S["ATTN_ERR_ALIGN"]
+    assert ew(lib, name, bias=BIAS + 4) == S["ATTN_ERR_ALIGN"]
+    assert ew(lib, name, y=Q + 1024) == S["ATTN_ERR_ALIAS"]      # partial overlap
+    assert ew(lib, name, bias=O + 64) == S["ATTN_ERR_ALIAS"]     # bias inside y
 
 
 DO, DQ, DK, DV = (A + i * GAP for i in range(6, 10))

@@ -3,11 +3,11 @@ backward oracle on the same seeded inputs.
 
 Tolerance, per gradient tensor over every checked element: max|dX| <=
 BWD_MAX * max|dX_ref| and ||dX||_2 <= BWD_RMS * ||dX_ref||_2.  The kernel's
-arithmetic bounds it: the probabilities and dS feed the MFMAs as bf16 (relative
-rounding 2^-9 each), D = rowsum(dO o O) uses the bf16-rounded forward output,
-products accumulate in fp32 and the gradients are rounded to bf16 (2^-9); the
-per-element errors are a few 2^-9 (~2e-3 each) of the typical gradient
-magnitude.  Measured on MI355X: normwise 2.0-2.7e-3, max 2-5e-3 of the largest
+arithmetic bounds it: the probabilities and dS feed the MFMAs as bf16 (round
+to nearest, at most 2^-8 relative each), D = rowsum(dO o O) uses the
+bf16-rounded forward output, products accumulate in fp32 and the gradients
+are rounded to bf16 (at most 2^-8); the per-element errors are a few 2^-9 to
+2^-8 (2-4e-3 each) of the typical gradient magnitude.  Measured on MI355X: normwise 2.0-2.7e-3, max 2-5e-3 of the largest
 gradient, so the bounds below keep a margin of about four.  Where the reference gradient vanishes (one key
 gives dQ = dK = 0 exactly, while the kernel leaves rounding residue of order
 1e-7), the comparison is absolute: denominators are floored at ABS_FLOOR.

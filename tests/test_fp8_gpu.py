@@ -18,7 +18,8 @@ which the tests check element by element as
 
     |dO_ic| <= (2^-4 + 2^-10) A_ic + B_ic + 2^-8 |O_ic| + 1e-6
 
-(the extra 2^-10 A and the doubled bf16 half-ulp absorb fp32 accumulation).
+(2^-8 |O| is the bf16 rounding of O, an 8-bit significand; the extra
+2^-10 A absorbs fp32 accumulation).
 The weights p come from the oracle.  lse comes from fp32 scores and sums:
 |dlse| <= 1e-3 as for the bf16 kernel.
 """
