@@ -22,7 +22,9 @@ Prints ONE JSON line.  Besides the headline value it carries:
                    causal 32k shapes, against the fp8 dense MFMA peak;
   masked        -- attn_fwd_masked: dense 8k with an [N, N] fp32 bias, and
                    causal 32k with a 4096-key sliding window (FLOPs counted
-                   over allowed (query, key) pairs only).
+                   over allowed (query, key) pairs only);
+  fusion        -- the elementwise chain relu(scale*x + bias) on a 512 MiB
+                   bf16 tensor, fused vs three launches, against HBM peak.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--quick]
 """
@@ -203,6 +205,28 @@ def masked_legs(ea, workloads, steps, warmup):
         log(f"[bench] masked {name} window={window} bias={with_bias}: {ms:.4f} ms, {rec['TFLOP/s']} TFLOP/s")
         del q, k, v, o, lse, bias
         torch.cuda.empty_cache()
+    return out
+
+
+def fusion_leg(ea, steps, warmup):
+    import torch
+    from exact_attention_124_amd.workloads import make_chain
+    rows, cols = 65536, 4096
+    x, b = make_chain(rows, cols, seed=0, device="cuda")
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    nbytes = x.numel() * 2
+    out = {"shape": [rows, cols], "dtype": "bf16", "tensor_bytes": nbytes}
+    for name, fn, crossings in (("fused", ea.ew_chain_fused, 2), ("unfused", ea.ew_chain_unfused, 6)):
+        tot, pl = time_launches(lambda: fn(x, y, b, 1.7, stream=stream), steps, warmup, stream)  # noqa
+        ms = sum(pl) / len(pl)
+        gbs = crossings * nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "algorithmic_bytes": crossings * nbytes, "GB/s": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] fusion {name}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    out["fused_speedup"] = round(out["unfused"]["ms"] / out["fused"]["ms"], 2)
+    del x, y, b
+    torch.cuda.empty_cache()
     return out
 
 
@@ -389,6 +413,7 @@ def main():
         result["backward"] = bwd
         result["fp8"] = fp8_legs(ea, WORKLOADS, 10, 3)
         result["masked"] = masked_legs(ea, WORKLOADS, 10, 3)
+        result["fusion"] = fusion_leg(ea, 20, 5)
 
         if not args.no_cpu:
             log("[bench] timing the CPU oracle on a bounded sample")
