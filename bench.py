@@ -158,6 +158,22 @@ def bench_fp8(ea, w, steps, warmup):
     return total_ms, per
 
 
+def backward_legs(ea, workloads, steps, warmup):
+    bwd = []
+    for name in (HEADLINE, "causal_32k_qx8_bf16"):
+        ww = workloads[name]
+        tot, pl = bench_backward(ea, ww, steps, warmup)
+        bm = sum(pl) / len(pl)
+        alg = 2.5 * ww.flops  # five products of 2*N^2*d per (b, h), halved when causal
+        bwd.append({"workload": name, "ms": round(bm, 3),
+                    "TFLOP/s": round(alg / (bm * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(alg / (bm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "flop_convention": "10*B*H*N^2*d (halved when causal); the kernels execute "
+                                       "14*B*H*N^2*d (S and dP are recomputed for dQ)"})
+        log(f"[bench] backward {name}: {bm:.3f} ms, {bwd[-1]['TFLOP/s']} TFLOP/s")
+    return bwd
+
+
 def fp8_legs(ea, workloads, steps, warmup):
     out = []
     for name in (HEADLINE, "causal_32k_qx8_bf16"):
@@ -299,6 +315,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only the backward legs (for kernel traces of the backward launches)")
     ap.add_argument("--masked-only", action="store_true",
                     help="only the masked / biased forward legs")
     ap.add_argument("--fp8-only", action="store_true",
@@ -324,6 +342,9 @@ def main():
 
     if args.n_sweep:
         n_sweep(ea)
+        return
+    if args.bwd_only:
+        print(json.dumps({"backward": backward_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
         return
     if args.masked_only:
         print(json.dumps({"masked": masked_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
@@ -398,19 +419,7 @@ def main():
                              "fused_speedup": round(um / launch_ms, 2)}
         log(f"[bench] unfused: {um:.3f} ms, {result['unfused']['GB/s']} GB/s")
 
-        bwd = []
-        for name in (HEADLINE, "causal_32k_qx8_bf16"):
-            ww = WORKLOADS[name]
-            tot, pl = bench_backward(ea, ww, 5, 2)
-            bm = sum(pl) / len(pl)
-            alg = 2.5 * ww.flops  # five products of 2*N^2*d per (b, h), halved when causal
-            bwd.append({"workload": name, "ms": round(bm, 3),
-                        "TFLOP/s": round(alg / (bm * 1e-3) / 1e12, 2),
-                        "frac_bf16_peak": round(alg / (bm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                        "flop_convention": "10*B*H*N^2*d (halved when causal); the kernels execute "
-                                           "14*B*H*N^2*d (S and dP are recomputed for dQ)"})
-            log(f"[bench] backward {name}: {bm:.3f} ms, {bwd[-1]['TFLOP/s']} TFLOP/s")
-        result["backward"] = bwd
+        result["backward"] = backward_legs(ea, WORKLOADS, 5, 2)
         result["fp8"] = fp8_legs(ea, WORKLOADS, 10, 3)
         result["masked"] = masked_legs(ea, WORKLOADS, 10, 3)
         result["fusion"] = fusion_leg(ea, 20, 5)

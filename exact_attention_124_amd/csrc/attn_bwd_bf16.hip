@@ -14,8 +14,11 @@
 // Like the forward, nothing N x N reaches memory: P is recomputed tile by
 // tile from Q, K and the forward's log-sum-exp (P_ij = exp(s_ij - lse_i)).
 // Three launches on one stream, no atomics (the result is deterministic):
-//   1. stats: D_i = dO_i . O_i and lse_i * log2(e) (fp32, into the caller's
-//      workspace, rows padded to a multiple of 32 with zeros);
+//   1. stats: -lse_i / scale and -D_i, D_i = dO_i . O_i (fp32, into the
+//      caller's workspace, rows padded to a multiple of 32 with zeros); the
+//      dK/dV kernel loads them straight into its S and dP accumulators as the
+//      MFMAs' starting values, so S' = S - lse/scale and dP' = dP - D come out
+//      of the matrix cores and P = exp2(scale log2(e) S'), dS = P dP';
 //   2. dK/dV: a workgroup owns 128 keys (four waves of 32), keeps their K and
 //      V rows in VGPRs and streams 32-query tiles of Q, dO through LDS;
 //   3. dQ:   a workgroup owns 128 queries, keeps their Q and dO rows in VGPRs
@@ -36,7 +39,7 @@ namespace bwd_bf16 {
 struct Params {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;   // forward log-sum-exp (natural log), [BH, N]
-    float *stats;       // workspace [BH][2][Npad]: lse * log2(e), then D; zero past N
+    float *stats;       // workspace [BH][2][Npad]: -lse / scale, then -D; zero past N
     int Npad;           // N rounded up to a multiple of 32
     uint16_t *dq, *dk, *dv;
     int N;
@@ -110,13 +113,13 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float mu
 }
 
 // ---------------------------------------------------------------------------
-// 1. Row statistics: lse_i * log2(e) and D_i = dO_i . O_i, 16 lanes per row,
-//    over the padded rows of every slice (zeros past N).
+// 1. Row statistics: -lse_i / scale and -D_i, D_i = dO_i . O_i, 16 lanes per
+//    row, over the padded rows of every slice (zeros past N).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout,
                                                     const float *__restrict__ lse, float *__restrict__ stats, int N,
-                                                    int Npad, long long prow_total) {
+                                                    int Npad, long long prow_total, float scale) {
     constexpr int PER = D / 16;  // elements per lane
     const long long prow = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);  // padded row
     const int l16 = threadIdx.x & 15;
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__
     for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
     if (prow < prow_total && l16 == 0) {
         float *st = stats + bh * 2 * Npad;
-        st[r] = live ? lse[row] * kLog2e : 0.f;
-        st[Npad + r] = acc;
+        st[r] = live ? -lse[row] / scale : 0.f;
+        st[Npad + r] = -acc;
     }
 }
 
@@ -171,7 +174,13 @@ void dkdv_kernel(Params p) {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = logical / p.nblk;
     const int kb = logical - bh * p.nblk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Non-causal: readfirstlane tells the compiler the wave index is uniform,
+    // which makes the edge-tile test a scalar branch that interior tiles
+    // skip.  Causal (where edge tiles are common): left as is, the test is
+    // folded into the probability loop as selects, which keeps fewer values
+    // live than a branch around it and avoids spilling.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int N = p.N;
 
@@ -234,23 +243,21 @@ void dkdv_kernel(Params p) {
         if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
         if (active(i)) {
             const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
-            // Statistics of this lane's query rows 32*qb + 8*g + 4*hf + 0..3
-            // (within the padded rows, so every 16-byte load is in range).
-            f32x4 lse4[NQB][4], dl4[NQB][4];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t off = (uint32_t)(i * BQ + 32 * qb + 8 * g + 4 * hf) * 4u;
-                    lse4[qb][g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
-                    dl4[qb][g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
-                }
-            }
+            // Accumulator starting values: -lse/scale and -D of this lane's
+            // query rows 32*qb + 8*g + 4*hf + 0..3, four rows per 16-byte load
+            // (within the padded rows, so every load is in range).
             f32x16 s[NQB], dp[NQB];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
-                s[qb] = f32x16{};
-                dp[qb] = f32x16{};
+                f32x4 a[4], b[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t off = (uint32_t)(i * BQ + 32 * qb + 8 * g + 4 * hf) * 4u;
+                    a[g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
+                    b[g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
+                }
+                s[qb] = __builtin_bit_cast(f32x16, a);
+                dp[qb] = __builtin_bit_cast(f32x16, b);
             }
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
@@ -260,22 +267,48 @@ void dkdv_kernel(Params p) {
                     dp[qb] = mfma32(row_operand<D>(Os, 32 * qb, st, lane), vf[st], dp[qb]);
                 }
             }
-            // P = exp(scale*s - lse), dS = P (dP - D); masked entries are 0.
+            // P = exp2(c S'), dS = P dP'; pairs past the sequence end or above
+            // the causal diagonal get P = 0.  Causal: the test sits inside the
+            // loop (evaluated as selects on every tile, which keeps the fewest
+            // values live); non-causal: only the ragged last tile needs it, in
+            // a block of its own that every other tile branches around.
             const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
             bf16x8 pb[2 * NQB], db[2 * NQB];
+            if constexpr (CAUSAL) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
+                for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pr = fast_exp2(fmaf(s[qb][r], c, -lse4[qb][r >> 2][r & 3]));
-                    if (edge) {
-                        const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if (qi >= N || (CAUSAL && key > qi)) pr = 0.f;
+                    for (int r = 0; r < 16; ++r) {
+                        float pr = fast_exp2(s[qb][r] * c);
+                        if (edge) {
+                            const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            if (qi >= N || key > qi) pr = 0.f;
+                        }
+                        pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
+                        db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
                     }
-                    const float ds = pr * (dp[qb][r] - dl4[qb][r >> 2][r & 3]);
-                    pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
-                    db[2 * qb + (r >> 3)][r & 7] = (__bf16)ds;
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(s[qb][r] * c);
+                if (edge) {
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            if (qi >= N) s[qb][r] = 0.f;
+                        }
                 }
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float pr = s[qb][r];
+                        pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
+                        db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
+                    }
             }
             // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
 #pragma unroll
@@ -316,7 +349,7 @@ void dq_kernel(Params p) {
     const int bh = logical / p.nblk;
     int qb = logical - bh * p.nblk;
     if (CAUSAL) qb = p.nblk - 1 - qb;  // longest rows first
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int N = p.N;
 
@@ -342,8 +375,8 @@ void dq_kernel(Params p) {
     }
     const bool live = qrow < N;
     const float *stq = p.stats + (size_t)bh * 2 * p.Npad;
-    const float lse2 = live ? stq[qrow] : 0.f;
-    const float dlt = live ? stq[p.Npad + qrow] : 0.f;
+    const float nlse2 = live ? stq[qrow] * p.scale_log2 : 0.f;  // -lse * log2(e)
+    const float ndlt = live ? stq[p.Npad + qrow] : 0.f;           // -D
 
     int ntiles = (N + BC - 1) / BC;
     int nfull = N / BC;
@@ -399,12 +432,12 @@ void dq_kernel(Params p) {
             for (int b = 0; b < 2; ++b) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pr = fast_exp2(fmaf(s[b][r], c, -lse2));
+                    float pr = fast_exp2(fmaf(s[b][r], c, nlse2));
                     if (masked) {
                         const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
                         if (kk > lim) pr = 0.f;
                     }
-                    db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] - dlt));
+                    db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] + ndlt));
                 }
             }
             // dQ^T += K^T dS^T (scale applied at the end).
@@ -447,15 +480,14 @@ hipError_t launch(const BwdArgs &a, hipStream_t s) {
     p.scale_log2 = a.scale * kLog2e;
     const long long prows = (long long)a.BH * p.Npad;
     hipLaunchKernelGGL((stats_kernel<D>), dim3((unsigned)((prows + 15) / 16)), dim3(256), 0, s, p.o, p.dout,
-                       p.lse, p.stats, a.N, p.Npad, prows);
+                       p.lse, p.stats, a.N, p.Npad, prows, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // d=128: non-causal runs two waves per SIMD (10 % faster at dense 8k even
-    // though the 256-register budget spills a few values); causal keeps one
-    // wave per SIMD with 64-query tiles (9 % faster at causal 2k).
-    if (D == 128 && !CAUSAL) e = launch_dkdv<D, CAUSAL, 4, 32, 2>(p, a, s);
-    else if (D == 128) e = launch_dkdv<D, CAUSAL, 4, 64, 1>(p, a, s);
-    else e = launch_dkdv<D, CAUSAL, 4, 32, 1>(p, a, s);
+    // Two waves per SIMD: d=128 with 32-query tiles (the 256-register budget
+    // spills a few values, still 20-30 % faster than one wave per SIMD),
+    // d=64 with 64-query tiles.
+    if constexpr (D == 128) e = launch_dkdv<D, CAUSAL, 4, 32, 2>(p, a, s);
+    else e = launch_dkdv<D, CAUSAL, 4, 64, 2>(p, a, s);
     if (e != hipSuccess) return e;
     p.nblk = (a.N + 127) / 128;
     const unsigned blocks = (unsigned)a.BH * (unsigned)p.nblk;

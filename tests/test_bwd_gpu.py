@@ -88,7 +88,8 @@ def test_backward_gpt2_heads_full(ea, W, oracle_mod):
     check(gpu_grads(ea, q, k, v, g, w.causal), ref, "gpt2 heads")
 
 
-@pytest.mark.parametrize("name,nslices,nsamp", [("causal_2k_bf16", 2, 64), ("dense_8k_bf16", 1, 32)])
+@pytest.mark.parametrize("name,nslices,nsamp", [("causal_2k_bf16", 2, 64), ("dense_8k_bf16", 1, 32),
+                                                 ("causal_32k_qx8_bf16", 1, 16)])
 def test_backward_sampled(ea, W, oracle_mod, name, nslices, nsamp):
     w = W.WORKLOADS[name]
     say(f"[bwd] {w.describe()} (sampled rows and keys)")
