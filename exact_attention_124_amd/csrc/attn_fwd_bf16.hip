@@ -276,6 +276,9 @@ void kernel(Params p) {
         __syncthreads();
         f32x16 sa[NB], sb[NB];
         if (active(0)) scores(0, sa);
+        // The first step refills K buffer 0 (tile 2); every wave must have
+        // finished reading tile 0 from it first.
+        __syncthreads();
         auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
             if (j + 2 < ntiles) load_k(j + 2, j & 1);
             if (j + 1 < ntiles) {
