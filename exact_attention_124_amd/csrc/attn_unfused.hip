@@ -15,6 +15,8 @@
 // 16-byte coalesced row accesses); the point of the path is its traffic.
 #include "common.h"
 #include "launch.h"
+#define ATTN_FWD_BF16_NO_DEFAULT_LAUNCHER
+#include "attn_fwd_bf16.hip"  // LDS layout of V tiles (Layout<D>)
 
 namespace attn {
 namespace {
@@ -232,10 +234,147 @@ __global__ __launch_bounds__(256) void softmax_rows_bf16_stream_kernel(uint16_t 
 }
 
 // ---------------------------------------------------------------------------
-// 3. Output, bf16: O = P V.  O^T = V^T P^T on the 32x32x16 MFMA; V tiles are
-//    transposed into LDS (double-buffered), each wave streams its own 32 rows
-//    of P straight from memory into B-operand registers.
+// 3. Output, bf16: O = P V.  O^T = V^T P^T on the 32x32x16 MFMA.
+//
+// pv_ring_kernel (N a multiple of 8): 256 query rows per workgroup; tiles of
+// 64 keys of P (256 rows x 128 B) and V (64 rows of D) go from memory straight
+// into LDS through a ring of three slots, so two tiles are in flight while one
+// is multiplied.  P is the one N x N read of this launch, and a tile fetched
+// only one ahead leaves each iteration waiting a full memory latency.
+//
+// The direct-to-LDS loads are issued from inline assembly: the compiler counts
+// its own such loads as writes to all of LDS that every workgroup barrier (a
+// release fence) and every LDS read must wait for, which would drain the whole
+// ring each iteration.  Completion is tracked here instead: a wave waits until
+// at most the loads of the newer tiles are outstanding (vector-memory loads
+// complete in order) and then meets the barrier.  M0, which holds the LDS
+// destination, is saved and restored around each load.
 // ---------------------------------------------------------------------------
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | (((N_ >> 4) & 3) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void load16_lds_async(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r)
+        : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,
+                                                      uint16_t *__restrict__ O, int N, int nqb) {
+    using VL = fwd_bf16::Layout<D>;
+    constexpr int WAVES = 8, BK = 64, STAGES = 3;
+    constexpr int BR = 32 * WAVES;            // query rows per workgroup
+    constexpr int PT = BR * BK;               // P tile elements (32 KiB)
+    constexpr int VT = BK * D;                // V tile elements
+    constexpr int SLOT = PT + VT;
+    constexpr int PLW = PT * 2 / 1024 / WAVES;  // 1 KiB loads per wave per tile
+    constexpr int VLW = VT * 2 / 1024 / WAVES;
+    constexpr int LPT = PLW + VLW;
+    static_assert(PLW * WAVES * 1024 == PT * 2 && VLW * WAVES * 1024 == VT * 2, "tile loads must split evenly");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * SLOT];
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = logical / nqb;
+    const int qb = logical - bh * nqb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int r0 = qb * BR;
+    const int nrow = min(BR, N - r0);
+    // P rows r0 .. r0 + nrow - 1 of this slice; reads past them return zero.
+    const auto rp = make_rsrc(P + ((size_t)bh * N + r0) * (size_t)N, (uint32_t)nrow * (uint32_t)N * 2u);
+    const auto rv = make_rsrc(V + (size_t)bh * N * D, (uint32_t)N * D * 2u);
+    const auto ro = make_rsrc(O + (size_t)bh * N * D, (uint32_t)N * D * 2u);
+
+    // P tile in LDS: row r (128 B = 8 chunks of 16 B), chunk pc stored at
+    // position pc ^ (r & 7) so the operand reads of 32 rows spread over banks.
+    // Load n of wave w fills LDS chunks 64 (w + WAVES n) .. +63.
+    uint32_t p_off[PLW], v_off[VLW];
+#pragma unroll
+    for (int n = 0; n < PLW; ++n) {
+        const int c = (wave + WAVES * n) * 64 + lane;
+        const int row = c >> 3, pc = (c & 7) ^ (row & 7);
+        p_off[n] = (uint32_t)(row * N + 8 * pc) * 2u;
+    }
+#pragma unroll
+    for (int n = 0; n < VLW; ++n) v_off[n] = VL::v_src((wave + WAVES * n) * 64 + lane);
+    auto load_tile = [&](int tile, int slot) __attribute__((always_inline)) {
+        uint16_t *Ps = smem + slot * SLOT;
+        uint16_t *Vs = Ps + PT;
+        const uint32_t pbase = (uint32_t)(tile * BK) * 2u;
+        const uint32_t vbase = (uint32_t)(tile * BK * D) * 2u;
+#pragma unroll
+        for (int n = 0; n < PLW; ++n) load16_lds_async(rp, pbase + p_off[n], Ps + (wave + WAVES * n) * 512);
+#pragma unroll
+        for (int n = 0; n < VLW; ++n) load16_lds_async(rv, vbase + v_off[n], Vs + (wave + WAVES * n) * 512);
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    const int ntiles = (N + BK - 1) / BK;
+    const int prow = wave * 32 + l32;  // this lane's row within the block
+    const int sw = prow & 7;
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+        if (t < ntiles) load_tile(t, t);
+    for (int jt = 0; jt < ntiles; ++jt) {
+        // Tile jt has landed once at most the next tile's loads are pending.
+        if (jt + 1 < ntiles) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // tile jt visible to all; every wave is done with tile jt - 1
+        if (jt + STAGES - 1 < ntiles) load_tile(jt + STAGES - 1, (jt + STAGES - 1) % STAGES);
+        const uint16_t *Ps = smem + (jt % STAGES) * SLOT;
+        const uint16_t *Vs = Ps + PT;
+#pragma unroll
+        for (int st = 0; st < BK / 16; ++st) {
+            // P^T operand: keys 16 st + 4 hf + 0..3 and 16 st + 8 + 4 hf + 0..3 (the
+            // key order of the V^T operand).  Keys at or past N (the ragged last
+            // tile) read the next row or zero; they are cleared here.
+            const int key = jt * BK + 16 * st;
+            u32x2 lo = *reinterpret_cast<const u32x2 *>(Ps + prow * BK + 8 * ((2 * st) ^ sw) + 4 * hf);
+            u32x2 hi = *reinterpret_cast<const u32x2 *>(Ps + prow * BK + 8 * ((2 * st + 1) ^ sw) + 4 * hf);
+            if (key >= N) lo = u32x2{0u, 0u};
+            if (key + 8 >= N) hi = u32x2{0u, 0u};
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            const bf16x8 pop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+                const i16x4 a0 = lds_read_tr16(Vs + VL::v_read(st, t, 0, lane));
+                const i16x4 a1 = lds_read_tr16(Vs + VL::v_read(st, t, 1, lane));
+                const i16x4 av[2] = {a0, a1};
+                acc[t] = mfma32(__builtin_bit_cast(bf16x8, av), pop, acc[t]);
+            }
+        }
+    }
+    const int qrow = r0 + prow;
+    if (qrow < N) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(acc[t][4 * g], acc[t][4 * g + 1]);
+                w[1] = pack_bf16x2(acc[t][4 * g + 2], acc[t][4 * g + 3]);
+                buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+            }
+        }
+    }
+}
+
+// pv_bf16_kernel (any N): V tiles are transposed into LDS (double-buffered),
+// each wave streams its own 32 rows of P straight from memory into B-operand
+// registers.
 template <int D, bool VEC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pv_bf16_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,
@@ -465,8 +604,9 @@ hipError_t launch_bf16(const FwdArgs &a, void *ws, hipStream_t s) {
     if (e != hipSuccess) return e;
 
     const unsigned g3 = (unsigned)a.BH * (unsigned)nqb;
+    const int nqr = (N + 255) / 256;
     if (vec)
-        hipLaunchKernelGGL((pv_bf16_kernel<D, true>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb);
+        hipLaunchKernelGGL((pv_ring_kernel<D>), dim3((unsigned)a.BH * (unsigned)nqr), dim3(512), 0, s, S, v, o, N, nqr);
     else
         hipLaunchKernelGGL((pv_bf16_kernel<D, false>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb);
     return hipGetLastError();
