@@ -156,12 +156,19 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _launch(device, fn, *args):
+    """Call a C entry point with ``device`` current: its kernels are launched
+    on the current device, which must own the tensors and the stream."""
+    with _torch().cuda.device(device):
+        return fn(*args)
+
+
 def _fwd(name, dtype, q, k, v, o, lse, causal, scale, stream):
     B, H, N, d = _check_qkv(q, k, v, dtype)
     _check_out(o, lse, (B, H, N, d), dtype, q.device)
     fn = getattr(load_library(), name)
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-            B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    st = _launch(q.device, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, name)
 
@@ -173,9 +180,9 @@ def _unfused(name, dtype, elem, q, k, v, o, lse, workspace, causal, scale, strea
         raise ValueError("workspace must be a contiguous tensor on q's device")
     nbytes = workspace.numel() * workspace.element_size()
     fn = getattr(load_library(), name)
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-            workspace.data_ptr(), nbytes, B, H, N, d, _scale(scale, d), 1 if causal else 0,
-            _stream(stream, q.device))
+    st = _launch(q.device, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                 workspace.data_ptr(), nbytes, B, H, N, d, _scale(scale, d), 1 if causal else 0,
+                 _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, name)
 
@@ -210,9 +217,10 @@ def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False,
     torch = _torch()
     B, H, N, d = _check_qkv(q, k, v, torch.float8_e4m3fn)
     _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
-    st = load_library().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-                                     B, H, N, d, _scale(scale, d), float(q_descale), float(k_descale),
-                                     float(v_descale), 1 if causal else 0, _stream(stream, q.device))
+    st = _launch(q.device, load_library().attn_fwd_fp8,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                 B, H, N, d, _scale(scale, d), float(q_descale), float(k_descale),
+                 float(v_descale), 1 if causal else 0, _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, "attn_fwd_fp8")
 
@@ -244,9 +252,10 @@ def attn_fwd_masked(q, k, v, o, lse=None, causal=False, window=(-1, -1), bias=No
     _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
     bp, sb, sh, si = _bias_view(bias, B, H, N, q.device)
     wl, wr = (int(window[0]), int(window[1]))
-    st = load_library().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-                                        B, H, N, d, _scale(scale, d), 1 if causal else 0, wl, wr, bp, sb, sh, si,
-                                        _stream(stream, q.device))
+    st = _launch(q.device, load_library().attn_fwd_masked,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, wl, wr, bp, sb, sh, si,
+                 _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, "attn_fwd_masked")
 
@@ -262,8 +271,9 @@ def _ew(name, x, y, bias, scale, stream):
     if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or tuple(bias.shape) != (x.shape[1],) \
             or not bias.is_contiguous() or bias.device != x.device:
         raise ValueError("bias must be a contiguous float32 [cols] tensor on x's device")
-    st = getattr(load_library(), name)(x.data_ptr(), y.data_ptr(), bias.data_ptr(), x.shape[0], x.shape[1],
-                                       float(scale), _stream(stream, x.device))
+    st = _launch(x.device, getattr(load_library(), name),
+                 x.data_ptr(), y.data_ptr(), bias.data_ptr(), x.shape[0], x.shape[1],
+                 float(scale), _stream(stream, x.device))
     if st != 0:
         raise AttnError(st, name)
 
@@ -299,10 +309,11 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=N
         raise ValueError("lse (the forward's log-sum-exp) is required")
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
-    st = load_library().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    st = _launch(q.device, load_library().attn_bwd,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, "attn_bwd")
 

@@ -315,7 +315,7 @@ const char *attn_status_string(int status) {
         case ATTN_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
         case ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, lse 4 bytes)";
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
-        case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_unfused_workspace_bytes()";
+        case ATTN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() reports";
         case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
         case ATTN_ERR_ARG: return "scale and fp8 descale factors must be finite and > 0, causal must be 0 or 1";
         default: return "unknown status";

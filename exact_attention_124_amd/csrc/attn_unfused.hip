@@ -372,10 +372,10 @@ __global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict
     }
 }
 
-// pv_bf16_kernel (any N): V tiles are transposed into LDS (double-buffered),
-// each wave streams its own 32 rows of P straight from memory into B-operand
-// registers.
-template <int D, bool VEC>
+// pv_bf16_kernel (N not a multiple of 8, so P rows are not 16-byte aligned):
+// V tiles are transposed into LDS (double-buffered), each wave gathers its own
+// 32 rows of P from memory into B-operand registers.
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pv_bf16_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,
                     uint16_t *__restrict__ O, int N, int nqb) {
@@ -413,13 +413,9 @@ void pv_bf16_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__
             const int j = key0 + 16 * st + 8 * hf;
             pst[st] = u32x4{0u, 0u, 0u, 0u};
             if (qrow < N && j < N) {
-                if (VEC) {
-                    pst[st] = *reinterpret_cast<const u32x4 *>(prow + j);
-                } else {
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
-                    for (int e = 0; e < 8 && j + e < N; ++e) w[e >> 1] |= (uint32_t)prow[j + e] << (16 * (e & 1));
-                    pst[st] = u32x4{w[0], w[1], w[2], w[3]};
-                }
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8 && j + e < N; ++e) w[e >> 1] |= (uint32_t)prow[j + e] << (16 * (e & 1));
+                pst[st] = u32x4{w[0], w[1], w[2], w[3]};
             }
         }
     };
@@ -608,7 +604,7 @@ hipError_t launch_bf16(const FwdArgs &a, void *ws, hipStream_t s) {
     if (vec)
         hipLaunchKernelGGL((pv_ring_kernel<D>), dim3((unsigned)a.BH * (unsigned)nqr), dim3(512), 0, s, S, v, o, N, nqr);
     else
-        hipLaunchKernelGGL((pv_bf16_kernel<D, false>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb);
+        hipLaunchKernelGGL((pv_bf16_kernel<D>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb);
     return hipGetLastError();
 }
 

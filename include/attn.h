@@ -53,7 +53,7 @@ typedef enum {
     ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                         */
     ATTN_ERR_ALIGN = 4,     /* q, k, v, o or workspace not 16-byte aligned; lse not 4-byte */
     ATTN_ERR_ALIAS = 5,     /* an output range overlaps an input or another output range   */
-    ATTN_ERR_WORKSPACE = 6, /* unfused workspace smaller than attn_unfused_workspace_bytes */
+    ATTN_ERR_WORKSPACE = 6, /* workspace smaller than attn_unfused_workspace_bytes / attn_bwd_workspace_bytes */
     ATTN_ERR_HIP = 7,       /* a HIP runtime call failed (see attn_last_hip_error)        */
     ATTN_ERR_ARG = 8        /* scale (or an fp8 descale) not finite and > 0, or causal not 0/1 */
 } attn_status;
