@@ -32,8 +32,9 @@
 //    reference maximum, so O = acc / l is unchanged; the probabilities stay
 //    below 2^8, well inside fp32 and bf16 range.
 //  * exp is exp2 with scale*log2(e) folded into one FMA; causal tiles above
-//    the diagonal are never loaded; causal query blocks run heaviest first;
-//    block ids are remapped so one head's query blocks share an XCD's L2.
+//    the diagonal are never loaded; a causal workgroup runs a long and a short
+//    query block (qb and nqb-1-qb), so all carry the same work; block ids are
+//    remapped so one head's query blocks share an XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -112,231 +113,238 @@ void kernel(Params p) {
     uint16_t *const Kbuf = smem;                // [2][TILE]
     uint16_t *const Vbuf = smem + 2 * T::TILE;  // [2][TILE]
 
+    // Causal: the workgroup runs query blocks nqb-1-item and item one after
+    // the other (the longer first), so every workgroup gets the same number
+    // of tiles and no long block starts last.
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nqb;
-    int qb = logical - bh * p.nqb;
-    if (CAUSAL) qb = p.nqb - 1 - qb;  // longest rows first
+    const int per = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
+    const int bh = logical / per;
+    const int item = logical - bh * per;
+    const int npass = (CAUSAL && p.nqb - 1 - item != item) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qb = CAUSAL ? (pass == 0 ? p.nqb - 1 - item : item) : item;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int hf = lane >> 5;
-    const int N = p.N;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int l32 = lane & 31;
+        const int hf = lane >> 5;
+        const int N = p.N;
 
-    const size_t slice = (size_t)bh * N * D;
-    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
-    const auto rq = make_rsrc(p.q + slice, slice_bytes);
-    const auto rk = make_rsrc(p.k + slice, slice_bytes);
-    const auto rv = make_rsrc(p.v + slice, slice_bytes);
-    const auto ro = make_rsrc(p.o + slice, slice_bytes);
+        const size_t slice = (size_t)bh * N * D;
+        const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+        const auto rq = make_rsrc(p.q + slice, slice_bytes);
+        const auto rk = make_rsrc(p.k + slice, slice_bytes);
+        const auto rv = make_rsrc(p.v + slice, slice_bytes);
+        const auto ro = make_rsrc(p.o + slice, slice_bytes);
 
-    const int r0 = qb * BR;         // first query row of this workgroup
-    const int q0 = r0 + wave * 32;  // first query row of this wave
-    const int qrow = q0 + l32;      // this lane's query row
+        const int r0 = qb * BR;         // first query row of this workgroup
+        const int q0 = r0 + wave * 32;  // first query row of this wave
+        const int qrow = q0 + l32;      // this lane's query row
 
-    // Q fragment (B operand of S^T = K Q^T): lane holds query qrow and head
-    // dims 16*s + 8*hf .. +7 for each 16-wide step s.  Rows >= N read as zero.
-    bf16x8 qf[D / 16];
+        // Q fragment (B operand of S^T = K Q^T): lane holds query qrow and head
+        // dims 16*s + 8*hf .. +7 for each 16-wide step s.  Rows >= N read as zero.
+        bf16x8 qf[D / 16];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
+        for (int s = 0; s < D / 16; ++s)
+            qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
 
-    // Tiles 0 .. ntiles-1 are visited; tiles 0 .. nfull-1 need no mask for
-    // any row of the workgroup.
-    int ntiles = (N + BC - 1) / BC;
-    int nfull = N / BC;
-    if (CAUSAL) {
-        ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
-        nfull = min(nfull, (r0 + 1) / BC);
-    }
+        // Tiles 0 .. ntiles-1 are visited; tiles 0 .. nfull-1 need no mask for
+        // any row of the workgroup.
+        int ntiles = (N + BC - 1) / BC;
+        int nfull = N / BC;
+        if (CAUSAL) {
+            ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+            nfull = min(nfull, (r0 + 1) / BC);
+        }
 
-    // ---- HBM -> LDS, 16 bytes per lane ----
-    // Wave-load `ins` fills LDS chunks [64*ins, 64*ins + 64); lane l writes
-    // chunk 64*ins + l.  Tiles past the end of the slice read as zero (buffer
-    // bounds), so loads need no guard.
-    uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
+        // ---- HBM -> LDS, 16 bytes per lane ----
+        // Wave-load `ins` fills LDS chunks [64*ins, 64*ins + 64); lane l writes
+        // chunk 64*ins + l.  Tiles past the end of the slice read as zero (buffer
+        // bounds), so loads need no guard.
+        uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
 #pragma unroll
-    for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
-        const int c = (wave + WAVES * n) * 64 + lane;
-        k_off[n] = L::k_src(c);
-        v_off[n] = L::v_src(c);
-    }
-    auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
+        for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
+            const int c = (wave + WAVES * n) * 64 + lane;
+            k_off[n] = L::k_src(c);
+            v_off[n] = L::v_src(c);
+        }
+        auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
 #pragma unroll
-        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
-            buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
-    };
-    auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+        };
+        auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
 #pragma unroll
-        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
-            buf_load16_lds(rv, base + v_off[n], Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
-    };
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                buf_load16_lds(rv, base + v_off[n], Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+        };
 
-    // ---- per-wave compute pieces ----
-    // S^T = K_tile Q^T, one 32x32 accumulator per 32-key block.
-    auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
-        const uint16_t *Ks = Kbuf + buf * T::TILE;
+        // ---- per-wave compute pieces ----
+        // S^T = K_tile Q^T, one 32x32 accumulator per 32-key block.
+        auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
+            const uint16_t *Ks = Kbuf + buf * T::TILE;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+            for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
+            for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    s[b] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, b, lane)), qf[st], s[b]);
+            }
+        };
+        // Causal: a tile with no key <= the wave's last row is skipped by the wave.
+        auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
+
+        // V^T operand for key step st and head-dim block t from two transpose
+        // reads: lane l receives head dim 32*t + l%32 at keys
+        // {16*st + 4*(l/32) + 0..3} (r = 0) and {16*st + 8 + 4*(l/32) + 0..3}
+        // (r = 1) -- the key order of the score accumulator's lane halves.
+        auto v_operand = [&](const uint16_t *Vs, int st, int t) __attribute__((always_inline)) {
+            const i16x4 lo = lds_read_tr16(Vs + L::v_read(st, t, 0, lane));
+            const i16x4 hi = lds_read_tr16(Vs + L::v_read(st, t, 1, lane));
+            const i16x4 w[2] = {lo, hi};
+            return __builtin_bit_cast(bf16x8, w);
+        };
+
+        const float c = p.scale_log2;
+        float m_run = -INFINITY;  // running reference max (log2 units) for query qrow
+        float l_run = 0.f;        // running sum over this lane's half of the keys
+        f32x16 acc[D / 32];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+        // Online softmax of score tile j: probabilities (bf16, B operand of the
+        // P*V product, pb[2b], pb[2b+1] for key block b) relative to the running
+        // reference maximum; the output accumulator is rescaled when it moves.
+        auto softmax = [&](int j, f32x16 (&s)[NB], bf16x8 (&pb)[2 * NB], bool masked) __attribute__((always_inline)) {
+            if (masked) {  // keys past the end of the sequence and, if causal, past the query
+                const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (kk > lim) s[b][r] = -INFINITY;
+                    }
+                }
+            }
+            float mx = s[0][0];
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                s[b] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, b, lane)), qf[st], s[b]);
-        }
-    };
-    // Causal: a tile with no key <= the wave's last row is skipped by the wave.
-    auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
-
-    // V^T operand for key step st and head-dim block t from two transpose
-    // reads: lane l receives head dim 32*t + l%32 at keys
-    // {16*st + 4*(l/32) + 0..3} (r = 0) and {16*st + 8 + 4*(l/32) + 0..3}
-    // (r = 1) -- the key order of the score accumulator's lane halves.
-    auto v_operand = [&](const uint16_t *Vs, int st, int t) __attribute__((always_inline)) {
-        const i16x4 lo = lds_read_tr16(Vs + L::v_read(st, t, 0, lane));
-        const i16x4 hi = lds_read_tr16(Vs + L::v_read(st, t, 1, lane));
-        const i16x4 w[2] = {lo, hi};
-        return __builtin_bit_cast(bf16x8, w);
-    };
-
-    const float c = p.scale_log2;
-    float m_run = -INFINITY;  // running reference max (log2 units) for query qrow
-    float l_run = 0.f;        // running sum over this lane's half of the keys
-    f32x16 acc[D / 32];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-
-    // Online softmax of score tile j: probabilities (bf16, B operand of the
-    // P*V product, pb[2b], pb[2b+1] for key block b) relative to the running
-    // reference maximum; the output accumulator is rescaled when it moves.
-    auto softmax = [&](int j, f32x16 (&s)[NB], bf16x8 (&pb)[2 * NB], bool masked) __attribute__((always_inline)) {
-        if (masked) {  // keys past the end of the sequence and, if causal, past the query
-            const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+                for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+            mx = pair_max(mx) * c;  // c > 0, so scaling commutes with max
+            // The reference maximum moves only when some row of the wave exceeds
+            // it by more than 2^kLazyThreshold.
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_safe);
+                m_run = m_safe;
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+            }
+            float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    if (kk > lim) s[b][r] = -INFINITY;
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
+                    const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
+                    rs0 += p0;
+                    rs1 += p1;
+                    pb[2 * b + (r >> 3)][r & 7] = (__bf16)p0;
+                    pb[2 * b + (r >> 3)][(r & 7) + 1] = (__bf16)p1;
                 }
             }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-        mx = pair_max(mx) * c;  // c > 0, so scaling commutes with max
-        // The reference maximum moves only when some row of the wave exceeds
-        // it by more than 2^kLazyThreshold.
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_safe);
-            m_run = m_safe;
-            l_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-        }
-        float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
-                const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
-                rs0 += p0;
-                rs1 += p1;
-                pb[2 * b + (r >> 3)][r & 7] = (__bf16)p0;
-                pb[2 * b + (r >> 3)][(r & 7) + 1] = (__bf16)p1;
-            }
-        }
-        l_run += rs0 + rs1;
-    };
-    // O^T += V_tile^T P^T.
-    auto pv = [&](int buf, const bf16x8 (&pb)[2 * NB]) __attribute__((always_inline)) {
-        const uint16_t *Vs = Vbuf + buf * T::TILE;
-#pragma unroll
-        for (int st = 0; st < BC / 16; ++st) {
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) acc[t] = mfma32(v_operand(Vs, st, t), pb[st], acc[t]);
-        }
-    };
-
-    if constexpr (KAHEAD) {
-        // During iteration j the LDS holds K(j+1) and V(j); K(j+2) and V(j+1)
-        // are in flight, into the buffers K(j) and V(j-1) have vacated.
-        load_k(0, 0);
-        load_v(0, 0);
-        if (ntiles > 1) load_k(1, 1);
-        wait_vmem();
-        __syncthreads();
-        f32x16 sa[NB], sb[NB];
-        if (active(0)) scores(0, sa);
-        // The first step refills K buffer 0 (tile 2); every wave must have
-        // finished reading tile 0 from it first.
-        __syncthreads();
-        auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
-            if (j + 2 < ntiles) load_k(j + 2, j & 1);
-            if (j + 1 < ntiles) {
-                load_v(j + 1, (j + 1) & 1);
-                if (active(j + 1)) scores((j + 1) & 1, nxt);
-            }
-            if (active(j)) {
-                bf16x8 pb[2 * NB];
-                softmax(j, cur, pb, j >= nfull);
-                pv(j & 1, pb);
-            }
-            wait_vmem();
-            __syncthreads();
+            l_run += rs0 + rs1;
         };
-        int j = 0;
-        for (; j + 1 < ntiles; j += 2) {
-            step(j, sa, sb);
-            step(j + 1, sb, sa);
-        }
-        if (j < ntiles) step(j, sa, sb);
-    } else {
-        load_k(0, 0);
-        load_v(0, 0);
-        wait_vmem();
-        __syncthreads();
-        for (int j = 0; j < ntiles; ++j) {
-            const int buf = j & 1;
-            if (j + 1 < ntiles) {
-                load_k(j + 1, buf ^ 1);
-                load_v(j + 1, buf ^ 1);
+        // O^T += V_tile^T P^T.
+        auto pv = [&](int buf, const bf16x8 (&pb)[2 * NB]) __attribute__((always_inline)) {
+            const uint16_t *Vs = Vbuf + buf * T::TILE;
+#pragma unroll
+            for (int st = 0; st < BC / 16; ++st) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) acc[t] = mfma32(v_operand(Vs, st, t), pb[st], acc[t]);
             }
-            if (active(j)) {
-                f32x16 s[NB];
-                bf16x8 pb[2 * NB];
-                scores(buf, s);
-                softmax(j, s, pb, j >= nfull);
-                pv(buf, pb);
-            }
+        };
+
+        if constexpr (KAHEAD) {
+            // During iteration j the LDS holds K(j+1) and V(j); K(j+2) and V(j+1)
+            // are in flight, into the buffers K(j) and V(j-1) have vacated.
+            load_k(0, 0);
+            load_v(0, 0);
+            if (ntiles > 1) load_k(1, 1);
             wait_vmem();
             __syncthreads();
-        }
-    }
-
-    // Epilogue: O = acc / l, lse = ln(2) * (m + log2 l).
-    const float l_tot = pair_sum(l_run);
-    const float inv = 1.f / l_tot;
-    if (qrow < N) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
-                buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+            f32x16 sa[NB], sb[NB];
+            if (active(0)) scores(0, sa);
+            // The first step refills K buffer 0 (tile 2); every wave must have
+            // finished reading tile 0 from it first.
+            __syncthreads();
+            auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
+                if (j + 2 < ntiles) load_k(j + 2, j & 1);
+                if (j + 1 < ntiles) {
+                    load_v(j + 1, (j + 1) & 1);
+                    if (active(j + 1)) scores((j + 1) & 1, nxt);
+                }
+                if (active(j)) {
+                    bf16x8 pb[2 * NB];
+                    softmax(j, cur, pb, j >= nfull);
+                    pv(j & 1, pb);
+                }
+                wait_vmem();
+                __syncthreads();
+            };
+            int j = 0;
+            for (; j + 1 < ntiles; j += 2) {
+                step(j, sa, sb);
+                step(j + 1, sb, sa);
+            }
+            if (j < ntiles) step(j, sa, sb);
+        } else {
+            load_k(0, 0);
+            load_v(0, 0);
+            wait_vmem();
+            __syncthreads();
+            for (int j = 0; j < ntiles; ++j) {
+                const int buf = j & 1;
+                if (j + 1 < ntiles) {
+                    load_k(j + 1, buf ^ 1);
+                    load_v(j + 1, buf ^ 1);
+                }
+                if (active(j)) {
+                    f32x16 s[NB];
+                    bf16x8 pb[2 * NB];
+                    scores(buf, s);
+                    softmax(j, s, pb, j >= nfull);
+                    pv(buf, pb);
+                }
+                wait_vmem();
+                __syncthreads();
             }
         }
-        if (hf == 0 && p.lse) p.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+
+        // Epilogue: O = acc / l, lse = ln(2) * (m + log2 l).
+        const float l_tot = pair_sum(l_run);
+        const float inv = 1.f / l_tot;
+        if (qrow < N) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+                    w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+                    buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+                }
+            }
+            if (hf == 0 && p.lse) p.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
     }
 }
 
@@ -352,7 +360,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.N = a.N;
     p.nqb = (a.N + T::BR - 1) / T::BR;
     p.scale_log2 = a.scale * kLog2e;
-    const unsigned blocks = (unsigned)a.BH * (unsigned)p.nqb;
+    const unsigned blocks = (unsigned)a.BH * (unsigned)(CAUSAL ? (p.nqb + 1) / 2 : p.nqb);
     hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }
