@@ -164,6 +164,40 @@ def test_causal_32k_qx8_bf16_sampled(ea, W, oracle_mod):
     _sampled(ea, W, oracle_mod, "causal_32k_qx8_bf16", 256, 4)
 
 
+def test_causal_odd_block_count_eight_waves(ea, W, oracle_mod):
+    # B*H*ceil(N/256) >= 1024 and N > 4096 select the 8-wave causal kernel; with
+    # N = 17 * 256 one workgroup of each slice runs the middle query block alone
+    # and the others run blocks 16-i and i.  Rows are taken from the first,
+    # middle and last blocks and from block boundaries.
+    B, H, N, d = 1, 64, 17 * 256, 128
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=77)
+    rows = [0, 1, 255, 256, 2047, 2048, 2049, 2200, 2303, 2304, 4095, 4096, 4200, N - 1]
+    slices = [0, 31, B * H - 1]
+    say(f"[parity] causal B={B} H={H} N={N} (17 query blocks of 256), rows {rows}")
+    qs, ks, vs = (t.reshape(-1, N, d)[slices] for t in (q, k, v))
+    ro, rl = oracle_mod.attention(qs, ks, vs, 1 / math.sqrt(d), True, rows=rows)
+    o, lse = ea.attention(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    sl, rw = torch.tensor(slices, device=o.device), torch.tensor(rows, device=o.device)
+    check_bf16(o.reshape(-1, N, d)[sl][:, rw], lse.reshape(-1, N)[sl][:, rw], ro, rl, "fused, odd block count")
+    assert torch.isfinite(o).all().item()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unfused_ring_shapes(ea, W, oracle_mod, d, causal):
+    # N a multiple of 8 takes the LDS-ring P*V kernel (256 query rows per
+    # workgroup, 64-key tiles): one tile, one exact block, ragged rows and keys
+    # (264, 520: 8 rows in the last block, 8 keys in the last tile), several
+    # blocks.
+    for N in [8, 256, 264, 520, 1032]:
+        q, k, v = W.make_qkv(1, 2, N, d, torch.bfloat16, seed=300 + N)
+        ro, rl = oracle_mod.attention(q, k, v, 1 / math.sqrt(d), causal)
+        say(f"[unfused ring] N={N} d={d} causal={causal}")
+        o, lse = run(ea, q, k, v, causal, variant="unfused")
+        check_bf16(o, lse, ro, rl, "unfused", unfused_lse_tol(q, k, 1 / math.sqrt(d)))
+
+
 # ---------------------------------------------------------------------------
 # Ragged and degenerate shapes, full outputs.
 # ---------------------------------------------------------------------------
