@@ -46,6 +46,7 @@ struct Params {
     int nblk;           // blocks per slice (keys for dK/dV, queries for dQ)
     float scale;
     float scale_log2;   // scale * log2(e)
+    int paired;         // causal: each workgroup runs blocks i and nblk-1-i
 };
 
 // Tiles read both row-wise (ds_read_b128 of one 16-byte chunk of 16
@@ -171,162 +172,172 @@ void dkdv_kernel(Params p) {
     uint16_t *const Qbuf = smem;             // [2][QT]
     uint16_t *const Obuf = smem + 2 * QT;    // [2][QT] (dO)
 
+    // Causal, paired: the workgroup runs key blocks item and nblk-1-item one
+    // after the other (low key blocks see the most queries), so every
+    // workgroup gets the same number of tiles.  Unpaired: one block, in
+    // ascending order, which is longest first.
+    const bool paired = CAUSAL && p.paired != 0;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nblk;
-    const int kb = logical - bh * p.nblk;
-    // Non-causal: readfirstlane tells the compiler the wave index is uniform,
-    // which makes the edge-tile test a scalar branch that interior tiles
-    // skip.  Causal (where edge tiles are common): left as is, the test is
-    // folded into the probability loop as selects, which keeps fewer values
-    // live than a branch around it and avoids spilling.
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, hf = lane >> 5;
-    const int N = p.N;
+    const int per = paired ? (p.nblk + 1) / 2 : p.nblk;  // workgroups per slice
+    const int bh = logical / per;
+    const int item = logical - bh * per;
+    const int npass = (paired && p.nblk - 1 - item != item) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int kb = (paired && pass == 1) ? p.nblk - 1 - item : item;
+        // Non-causal: readfirstlane tells the compiler the wave index is uniform,
+        // which makes the edge-tile test a scalar branch that interior tiles
+        // skip.  Causal (where edge tiles are common): left as is, the test is
+        // folded into the probability loop as selects, which keeps fewer values
+        // live than a branch around it and avoids spilling.
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l32 = lane & 31, hf = lane >> 5;
+        const int N = p.N;
 
-    const size_t slice = (size_t)bh * N * D;
-    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
-    const auto rq = make_rsrc(p.q + slice, slice_bytes);
-    const auto rk = make_rsrc(p.k + slice, slice_bytes);
-    const auto rv = make_rsrc(p.v + slice, slice_bytes);
-    const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
-    const auto rdk = make_rsrc(p.dk + slice, slice_bytes);
-    const auto rdv = make_rsrc(p.dv + slice, slice_bytes);
-    const float *st = p.stats + (size_t)bh * 2 * p.Npad;
-    const auto rlse = make_rsrc(st, (uint32_t)p.Npad * 4u);
-    const auto rdl = make_rsrc(st + p.Npad, (uint32_t)p.Npad * 4u);
+        const size_t slice = (size_t)bh * N * D;
+        const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+        const auto rq = make_rsrc(p.q + slice, slice_bytes);
+        const auto rk = make_rsrc(p.k + slice, slice_bytes);
+        const auto rv = make_rsrc(p.v + slice, slice_bytes);
+        const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
+        const auto rdk = make_rsrc(p.dk + slice, slice_bytes);
+        const auto rdv = make_rsrc(p.dv + slice, slice_bytes);
+        const float *st = p.stats + (size_t)bh * 2 * p.Npad;
+        const auto rlse = make_rsrc(st, (uint32_t)p.Npad * 4u);
+        const auto rdl = make_rsrc(st + p.Npad, (uint32_t)p.Npad * 4u);
 
-    const int k0 = kb * BK + wave * 32;  // first key of this wave
-    const int key = k0 + l32;            // this lane's key
+        const int k0 = kb * BK + wave * 32;  // first key of this wave
+        const int key = k0 + l32;            // this lane's key
 
-    // Resident K and V (B operands of S = Q K^T and dP = dO V^T): lane holds
-    // key `key`, columns 16*st + 8*hf .. +7.  Keys >= N read as zero.
-    bf16x8 kf[D / 16], vf[D / 16];
+        // Resident K and V (B operands of S = Q K^T and dP = dO V^T): lane holds
+        // key `key`, columns 16*st + 8*hf .. +7.  Keys >= N read as zero.
+        bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        const uint32_t off = (uint32_t)(key * D + 16 * st + 8 * hf) * 2u;
-        kf[st] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-        vf[st] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-    }
-
-    const int nqt = (N + BQ - 1) / BQ;
-    const int t0 = CAUSAL ? (kb * BK) / BQ : 0;  // first query tile that sees any key of the block
-    auto active = [&](int i) __attribute__((always_inline)) { return !CAUSAL || i * BQ + BQ - 1 >= k0; };
-
-    uint32_t ld_off[LPW];
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
-    auto load_tile = [&](int i, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(i * BQ * D) * 2u;
-#pragma unroll
-        for (int n = 0; n < LPW; ++n) {
-            buf_load16_lds(rq, base + ld_off[n], Qbuf + buf * QT + (wave + WAVES * n) * 512);
-            buf_load16_lds(rdo, base + ld_off[n], Obuf + buf * QT + (wave + WAVES * n) * 512);
+        for (int st = 0; st < D / 16; ++st) {
+            const uint32_t off = (uint32_t)(key * D + 16 * st + 8 * hf) * 2u;
+            kf[st] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+            vf[st] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
         }
-    };
 
-    const float c = p.scale_log2;
-    f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-        dk[t] = f32x16{};
-        dv[t] = f32x16{};
-    }
+        const int nqt = (N + BQ - 1) / BQ;
+        const int t0 = CAUSAL ? (kb * BK) / BQ : 0;  // first query tile that sees any key of the block
+        auto active = [&](int i) __attribute__((always_inline)) { return !CAUSAL || i * BQ + BQ - 1 >= k0; };
 
-    if (t0 < nqt) {
-        load_tile(t0, 0);
-        wait_vmem();
-        __syncthreads();
-    }
-    for (int i = t0; i < nqt; ++i) {
-        const int buf = (i - t0) & 1;
-        if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
-        if (active(i)) {
-            const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
-            // Accumulator starting values: -lse/scale and -D of this lane's
-            // query rows 32*qb + 8*g + 4*hf + 0..3, four rows per 16-byte load
-            // (within the padded rows, so every load is in range).
-            f32x16 s[NQB], dp[NQB];
+        uint32_t ld_off[LPW];
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                f32x4 a[4], b[4];
+        for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
+        auto load_tile = [&](int i, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(i * BQ * D) * 2u;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t off = (uint32_t)(i * BQ + 32 * qb + 8 * g + 4 * hf) * 4u;
-                    a[g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
-                    b[g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
-                }
-                s[qb] = __builtin_bit_cast(f32x16, a);
-                dp[qb] = __builtin_bit_cast(f32x16, b);
+            for (int n = 0; n < LPW; ++n) {
+                buf_load16_lds(rq, base + ld_off[n], Qbuf + buf * QT + (wave + WAVES * n) * 512);
+                buf_load16_lds(rdo, base + ld_off[n], Obuf + buf * QT + (wave + WAVES * n) * 512);
             }
+        };
+
+        const float c = p.scale_log2;
+        f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
+        for (int t = 0; t < D / 32; ++t) {
+            dk[t] = f32x16{};
+            dv[t] = f32x16{};
+        }
+
+        if (t0 < nqt) {
+            load_tile(t0, 0);
+            wait_vmem();
+            __syncthreads();
+        }
+        for (int i = t0; i < nqt; ++i) {
+            const int buf = (i - t0) & 1;
+            if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
+            if (active(i)) {
+                const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
+                // Accumulator starting values: -lse/scale and -D of this lane's
+                // query rows 32*qb + 8*g + 4*hf + 0..3, four rows per 16-byte load
+                // (within the padded rows, so every load is in range).
+                f32x16 s[NQB], dp[NQB];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    s[qb] = mfma32(row_operand<D>(Qs, 32 * qb, st, lane), kf[st], s[qb]);
-                    dp[qb] = mfma32(row_operand<D>(Os, 32 * qb, st, lane), vf[st], dp[qb]);
-                }
-            }
-            // P = exp2(c S'), dS = P dP'; pairs past the sequence end or above
-            // the causal diagonal get P = 0.  Causal: the test sits inside the
-            // loop (evaluated as selects on every tile, which keeps the fewest
-            // values live); non-causal: only the ragged last tile needs it, in
-            // a block of its own that every other tile branches around.
-            const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
-            bf16x8 pb[2 * NQB], db[2 * NQB];
-            if constexpr (CAUSAL) {
+                    f32x4 a[4], b[4];
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float pr = fast_exp2(s[qb][r] * c);
-                        if (edge) {
-                            const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            if (qi >= N || key > qi) pr = 0.f;
-                        }
-                        pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
-                        db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
+                    for (int g = 0; g < 4; ++g) {
+                        const uint32_t off = (uint32_t)(i * BQ + 32 * qb + 8 * g + 4 * hf) * 4u;
+                        a[g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
+                        b[g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
                     }
-            } else {
+                    s[qb] = __builtin_bit_cast(f32x16, a);
+                    dp[qb] = __builtin_bit_cast(f32x16, b);
+                }
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
+                for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(s[qb][r] * c);
-                if (edge) {
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        s[qb] = mfma32(row_operand<D>(Qs, 32 * qb, st, lane), kf[st], s[qb]);
+                        dp[qb] = mfma32(row_operand<D>(Os, 32 * qb, st, lane), vf[st], dp[qb]);
+                    }
+                }
+                // P = exp2(c S'), dS = P dP'; pairs past the sequence end or above
+                // the causal diagonal get P = 0.  Causal: the test sits inside the
+                // loop (evaluated as selects on every tile, which keeps the fewest
+                // values live); non-causal: only the ragged last tile needs it, in
+                // a block of its own that every other tile branches around.
+                const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
+                bf16x8 pb[2 * NQB], db[2 * NQB];
+                if constexpr (CAUSAL) {
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            if (qi >= N) s[qb][r] = 0.f;
+                            float pr = fast_exp2(s[qb][r] * c);
+                            if (edge) {
+                                const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                                if (qi >= N || key > qi) pr = 0.f;
+                            }
+                            pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
+                            db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
+                        }
+                } else {
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(s[qb][r] * c);
+                    if (edge) {
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                                if (qi >= N) s[qb][r] = 0.f;
+                            }
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float pr = s[qb][r];
+                            pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
+                            db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
                         }
                 }
+                // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
+                for (int st = 0; st < BQ / 16; ++st) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float pr = s[qb][r];
-                        pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
-                        db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
+                    for (int t = 0; t < D / 32; ++t) {
+                        dv[t] = mfma32(tr_operand<D>(Os, st, t, lane), pb[st], dv[t]);
+                        dk[t] = mfma32(tr_operand<D>(Qs, st, t, lane), db[st], dk[t]);
                     }
-            }
-            // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
-#pragma unroll
-            for (int st = 0; st < BQ / 16; ++st) {
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t) {
-                    dv[t] = mfma32(tr_operand<D>(Os, st, t, lane), pb[st], dv[t]);
-                    dk[t] = mfma32(tr_operand<D>(Qs, st, t, lane), db[st], dk[t]);
                 }
             }
+            wait_vmem();
+            __syncthreads();
         }
-        wait_vmem();
-        __syncthreads();
-    }
 
-    if (key < N) {
-        store_rows<D>(dk, p.scale, rdk, key, hf);
-        store_rows<D>(dv, 1.f, rdv, key, hf);
+        if (key < N) {
+            store_rows<D>(dk, p.scale, rdk, key, hf);
+            store_rows<D>(dv, 1.f, rdv, key, hf);
+        }
     }
 }
 
@@ -345,118 +356,126 @@ void dq_kernel(Params p) {
     uint16_t *const Kbuf = smem;           // [2][KT]
     uint16_t *const Vbuf = smem + 2 * KT;  // [2][KT]
 
+    // Causal: paired (query blocks nblk-1-item, then item) or one block,
+    // longest first, as in the forward.
+    const bool paired = CAUSAL && p.paired != 0;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nblk;
-    int qb = logical - bh * p.nblk;
-    if (CAUSAL) qb = p.nblk - 1 - qb;  // longest rows first
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, hf = lane >> 5;
-    const int N = p.N;
+    const int per = paired ? (p.nblk + 1) / 2 : p.nblk;  // workgroups per slice
+    const int bh = logical / per;
+    const int item = logical - bh * per;
+    const int npass = (paired && p.nblk - 1 - item != item) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qb = (CAUSAL && (!paired || pass == 0)) ? p.nblk - 1 - item : item;
+        const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l32 = lane & 31, hf = lane >> 5;
+        const int N = p.N;
 
-    const size_t slice = (size_t)bh * N * D;
-    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
-    const auto rq = make_rsrc(p.q + slice, slice_bytes);
-    const auto rk = make_rsrc(p.k + slice, slice_bytes);
-    const auto rv = make_rsrc(p.v + slice, slice_bytes);
-    const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
-    const auto rdq = make_rsrc(p.dq + slice, slice_bytes);
+        const size_t slice = (size_t)bh * N * D;
+        const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+        const auto rq = make_rsrc(p.q + slice, slice_bytes);
+        const auto rk = make_rsrc(p.k + slice, slice_bytes);
+        const auto rv = make_rsrc(p.v + slice, slice_bytes);
+        const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
+        const auto rdq = make_rsrc(p.dq + slice, slice_bytes);
 
-    const int r0 = qb * BR;
-    const int q0 = r0 + wave * 32;
-    const int qrow = q0 + l32;
+        const int r0 = qb * BR;
+        const int q0 = r0 + wave * 32;
+        const int qrow = q0 + l32;
 
-    // Resident Q and dO (B operands of S^T = K Q^T and dP^T = V dO^T).
-    bf16x8 qf[D / 16], of[D / 16];
+        // Resident Q and dO (B operands of S^T = K Q^T and dP^T = V dO^T).
+        bf16x8 qf[D / 16], of[D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        const uint32_t off = (uint32_t)(qrow * D + 16 * st + 8 * hf) * 2u;
-        qf[st] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-        of[st] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
-    }
-    const bool live = qrow < N;
-    const float *stq = p.stats + (size_t)bh * 2 * p.Npad;
-    const float nlse2 = live ? stq[qrow] * p.scale_log2 : 0.f;  // -lse * log2(e)
-    const float ndlt = live ? stq[p.Npad + qrow] : 0.f;           // -D
-
-    int ntiles = (N + BC - 1) / BC;
-    int nfull = N / BC;
-    if (CAUSAL) {
-        ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
-        nfull = min(nfull, (r0 + 1) / BC);
-    }
-    auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
-
-    uint32_t ld_off[LPW];
-#pragma unroll
-    for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
-    auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(j * BC * D) * 2u;
-#pragma unroll
-        for (int n = 0; n < LPW; ++n) {
-            buf_load16_lds(rk, base + ld_off[n], Kbuf + buf * KT + (wave + WAVES * n) * 512);
-            buf_load16_lds(rv, base + ld_off[n], Vbuf + buf * KT + (wave + WAVES * n) * 512);
+        for (int st = 0; st < D / 16; ++st) {
+            const uint32_t off = (uint32_t)(qrow * D + 16 * st + 8 * hf) * 2u;
+            qf[st] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+            of[st] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
         }
-    };
+        const bool live = qrow < N;
+        const float *stq = p.stats + (size_t)bh * 2 * p.Npad;
+        const float nlse2 = live ? stq[qrow] * p.scale_log2 : 0.f;  // -lse * log2(e)
+        const float ndlt = live ? stq[p.Npad + qrow] : 0.f;           // -D
 
-    const float c = p.scale_log2;
-    f32x16 dq[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) dq[t] = f32x16{};
-
-    load_tile(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-        if (active(j)) {
-            const uint16_t *Ks = Kbuf + buf * KT, *Vs = Vbuf + buf * KT;
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                s[b] = f32x16{};
-                dp[b] = f32x16{};
-            }
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    s[b] = mfma32(row_operand<D>(Ks, 32 * b, st, lane), qf[st], s[b]);
-                    dp[b] = mfma32(row_operand<D>(Vs, 32 * b, st, lane), of[st], dp[b]);
-                }
-            }
-            const bool masked = j >= nfull;
-            const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
-            bf16x8 db[4];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pr = fast_exp2(fmaf(s[b][r], c, nlse2));
-                    if (masked) {
-                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if (kk > lim) pr = 0.f;
-                    }
-                    db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] + ndlt));
-                }
-            }
-            // dQ^T += K^T dS^T (scale applied at the end).
-#pragma unroll
-            for (int st = 0; st < BC / 16; ++st) {
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(tr_operand<D>(Ks, st, t, lane), db[st], dq[t]);
-            }
+        int ntiles = (N + BC - 1) / BC;
+        int nfull = N / BC;
+        if (CAUSAL) {
+            ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+            nfull = min(nfull, (r0 + 1) / BC);
         }
+        auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
+
+        uint32_t ld_off[LPW];
+#pragma unroll
+        for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
+        auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(j * BC * D) * 2u;
+#pragma unroll
+            for (int n = 0; n < LPW; ++n) {
+                buf_load16_lds(rk, base + ld_off[n], Kbuf + buf * KT + (wave + WAVES * n) * 512);
+                buf_load16_lds(rv, base + ld_off[n], Vbuf + buf * KT + (wave + WAVES * n) * 512);
+            }
+        };
+
+        const float c = p.scale_log2;
+        f32x16 dq[D / 32];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) dq[t] = f32x16{};
+
+        load_tile(0, 0);
         wait_vmem();
         __syncthreads();
+        for (int j = 0; j < ntiles; ++j) {
+            const int buf = j & 1;
+            if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
+            if (active(j)) {
+                const uint16_t *Ks = Kbuf + buf * KT, *Vs = Vbuf + buf * KT;
+                f32x16 s[2], dp[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    s[b] = f32x16{};
+                    dp[b] = f32x16{};
+                }
+#pragma unroll
+                for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        s[b] = mfma32(row_operand<D>(Ks, 32 * b, st, lane), qf[st], s[b]);
+                        dp[b] = mfma32(row_operand<D>(Vs, 32 * b, st, lane), of[st], dp[b]);
+                    }
+                }
+                const bool masked = j >= nfull;
+                const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+                bf16x8 db[4];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float pr = fast_exp2(fmaf(s[b][r], c, nlse2));
+                        if (masked) {
+                            const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            if (kk > lim) pr = 0.f;
+                        }
+                        db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] + ndlt));
+                    }
+                }
+                // dQ^T += K^T dS^T (scale applied at the end).
+#pragma unroll
+                for (int st = 0; st < BC / 16; ++st) {
+#pragma unroll
+                    for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(tr_operand<D>(Ks, st, t, lane), db[st], dq[t]);
+                }
+            }
+            wait_vmem();
+            __syncthreads();
+        }
+        if (live) store_rows<D>(dq, p.scale, rdq, qrow, hf);
     }
-    if (live) store_rows<D>(dq, p.scale, rdq, qrow, hf);
 }
 
 template <int D, bool CAUSAL, int WAVES, int BQ, int OCC>
 hipError_t launch_dkdv(Params p, const BwdArgs &a, hipStream_t s) {
     p.nblk = (a.N + 32 * WAVES - 1) / (32 * WAVES);
-    const unsigned blocks = (unsigned)a.BH * (unsigned)p.nblk;
+    p.paired = CAUSAL && pair_causal_blocks((long long)a.BH * p.nblk, 2);
+    const unsigned blocks = (unsigned)a.BH * (unsigned)(p.paired ? (p.nblk + 1) / 2 : p.nblk);
     hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, WAVES, BQ, OCC>), dim3(blocks), dim3(64 * WAVES), 0, s, p);
     return hipGetLastError();
 }
@@ -490,7 +509,8 @@ hipError_t launch(const BwdArgs &a, hipStream_t s) {
     else e = launch_dkdv<D, CAUSAL, 4, 64, 2>(p, a, s);
     if (e != hipSuccess) return e;
     p.nblk = (a.N + 127) / 128;
-    const unsigned blocks = (unsigned)a.BH * (unsigned)p.nblk;
+    p.paired = CAUSAL && pair_causal_blocks((long long)a.BH * p.nblk, 2);
+    const unsigned blocks = (unsigned)a.BH * (unsigned)(p.paired ? (p.nblk + 1) / 2 : p.nblk);
     hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }

@@ -48,6 +48,7 @@ struct Params {
     int N;
     int nqb;           // query blocks per slice
     float scale_log2;  // scale * log2(e)
+    int paired;        // causal: each workgroup runs blocks nqb-1-i and i
 };
 
 template <int D, int WAVES, int BC_>
@@ -113,16 +114,17 @@ void kernel(Params p) {
     uint16_t *const Kbuf = smem;                // [2][TILE]
     uint16_t *const Vbuf = smem + 2 * T::TILE;  // [2][TILE]
 
-    // Causal: the workgroup runs query blocks nqb-1-item and item one after
-    // the other (the longer first), so every workgroup gets the same number
-    // of tiles and no long block starts last.
+    // Causal, paired: the workgroup runs query blocks nqb-1-item and item one
+    // after the other, so every workgroup gets the same number of tiles and no
+    // long block starts last.  Causal, unpaired: one block, longest first.
+    const bool paired = CAUSAL && p.paired != 0;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int per = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
+    const int per = paired ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
     const int bh = logical / per;
     const int item = logical - bh * per;
-    const int npass = (CAUSAL && p.nqb - 1 - item != item) ? 2 : 1;
+    const int npass = (paired && p.nqb - 1 - item != item) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
-        const int qb = CAUSAL ? (pass == 0 ? p.nqb - 1 - item : item) : item;
+        const int qb = (CAUSAL && (!paired || pass == 0)) ? p.nqb - 1 - item : item;
 
         const int tid = threadIdx.x;
         const int lane = tid & 63;
@@ -360,7 +362,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.N = a.N;
     p.nqb = (a.N + T::BR - 1) / T::BR;
     p.scale_log2 = a.scale * kLog2e;
-    const unsigned blocks = (unsigned)a.BH * (unsigned)(CAUSAL ? (p.nqb + 1) / 2 : p.nqb);
+    p.paired = CAUSAL && pair_causal_blocks((long long)a.BH * p.nqb, WAVES == 8 ? 1 : 2);
+    const unsigned blocks = (unsigned)a.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
     hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }

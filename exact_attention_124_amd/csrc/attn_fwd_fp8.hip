@@ -26,7 +26,7 @@
 //    the order in which the score accumulator holds its keys.
 //  * O = v_descale * acc / l, stored as bf16; lse as in the bf16 kernel.
 // Tiles are 128 keys, double-buffered in LDS (32 KiB per K or V tile pair at
-// d = 128); causal skipping, the heaviest-first order of causal query blocks
+// d = 128); causal skipping, the pairing of long and short causal query blocks
 // and the XCD remap follow the bf16 kernel.
 #include "common.h"
 #include "launch.h"
@@ -70,6 +70,7 @@ struct Params {
     int nqb;           // query blocks per slice
     float scale_log2;  // scale * q_descale * k_descale * log2(e)
     float v_descale;
+    int paired;        // causal: each workgroup runs blocks nqb-1-i and i
 };
 
 template <int D, int WAVES, int BC_>
@@ -141,199 +142,208 @@ void kernel(Params p) {
     uint8_t *const Kbuf = smem;                // [2][TILE]
     uint8_t *const Vbuf = smem + 2 * T::TILE;  // [2][TILE]
 
+    // Causal: paired (blocks nqb-1-item, then item) or one block, longest
+    // first, as in the bf16 kernel.
+    const bool paired = CAUSAL && p.paired != 0;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / p.nqb;
-    int qb = logical - bh * p.nqb;
-    if (CAUSAL) qb = p.nqb - 1 - qb;  // longest rows first
+    const int per = paired ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
+    const int bh = logical / per;
+    const int item = logical - bh * per;
+    const int npass = (paired && p.nqb - 1 - item != item) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qb = (CAUSAL && (!paired || pass == 0)) ? p.nqb - 1 - item : item;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int l32 = lane & 31;
-    const int hf = lane >> 5;
-    const int N = p.N;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int l32 = lane & 31;
+        const int hf = lane >> 5;
+        const int N = p.N;
 
-    const size_t slice = (size_t)bh * N * D;
-    const uint32_t in_bytes = (uint32_t)N * D;
-    const auto rq = make_rsrc(p.q + slice, in_bytes);
-    const auto rk = make_rsrc(p.k + slice, in_bytes);
-    const auto rv = make_rsrc(p.v + slice, in_bytes);
-    const auto ro = make_rsrc(p.o + slice, in_bytes * 2u);
+        const size_t slice = (size_t)bh * N * D;
+        const uint32_t in_bytes = (uint32_t)N * D;
+        const auto rq = make_rsrc(p.q + slice, in_bytes);
+        const auto rk = make_rsrc(p.k + slice, in_bytes);
+        const auto rv = make_rsrc(p.v + slice, in_bytes);
+        const auto ro = make_rsrc(p.o + slice, in_bytes * 2u);
 
-    const int r0 = qb * BR;
-    const int q0 = r0 + wave * 32;
-    const int qrow = q0 + l32;
+        const int r0 = qb * BR;
+        const int q0 = r0 + wave * 32;
+        const int qrow = q0 + l32;
 
-    // Q fragment (B operand of S^T = K Q^T): query qrow, head dims 64*st +
-    // 32*hf .. +31 for each contraction step st.  Rows >= N read as zero.
-    i32x8 qf[D / 64];
-#pragma unroll
-    for (int st = 0; st < D / 64; ++st) {
-        const uint32_t off = (uint32_t)(qrow * D + 64 * st + 32 * hf);
-        const u32x4 a = buf_load16(rq, off), b = buf_load16(rq, off + 16u);
-        const u32x4 w[2] = {a, b};
-        qf[st] = __builtin_bit_cast(i32x8, w);
-    }
-
-    int ntiles = (N + BC - 1) / BC;
-    int nfull = N / BC;
-    if (CAUSAL) {
-        ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
-        nfull = min(nfull, (r0 + 1) / BC);
-    }
-
-    // ---- HBM -> LDS, 16 bytes per lane; wave-load n of this wave fills LDS
-    // chunks [64*(wave + WAVES*n), +64).  Past-the-end rows read as zero.
-    uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
-#pragma unroll
-    for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
-        const int c = (wave + WAVES * n) * 64 + lane;
-        k_off[n] = L::k_src(c);
-        v_off[n] = L::v_src(c);
-    }
-    auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(tile * BC * D);
-#pragma unroll
-        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
-            if (T::LOADS % WAVES == 0 || wave + WAVES * n < T::LOADS)
-                buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 1024);
-    };
-    auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(tile * BC * D);
-#pragma unroll
-        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
-            if (T::LOADS % WAVES == 0 || wave + WAVES * n < T::LOADS)
-                buf_load16_lds(rv, base + v_off[n], Vbuf + buf * T::TILE + (wave + WAVES * n) * 1024);
-    };
-
-    auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
-        const uint8_t *Ks = Kbuf + buf * T::TILE;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+        // Q fragment (B operand of S^T = K Q^T): query qrow, head dims 64*st +
+        // 32*hf .. +31 for each contraction step st.  Rows >= N read as zero.
+        i32x8 qf[D / 64];
 #pragma unroll
         for (int st = 0; st < D / 64; ++st) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const u32x4 w[2] = {lds_read16(Ks + L::k_read(st, b, 0, lane)),
-                                    lds_read16(Ks + L::k_read(st, b, 1, lane))};
-                s[b] = mfma_f8(__builtin_bit_cast(i32x8, w), qf[st], s[b]);
-            }
+            const uint32_t off = (uint32_t)(qrow * D + 64 * st + 32 * hf);
+            const u32x4 a = buf_load16(rq, off), b = buf_load16(rq, off + 16u);
+            const u32x4 w[2] = {a, b};
+            qf[st] = __builtin_bit_cast(i32x8, w);
         }
-    };
-    auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
 
-    const float c = p.scale_log2;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+        int ntiles = (N + BC - 1) / BC;
+        int nfull = N / BC;
+        if (CAUSAL) {
+            ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+            nfull = min(nfull, (r0 + 1) / BC);
+        }
 
-    // Online softmax of score tile j.  pf[g] is the e4m3 B operand of the P*V
-    // product for 64-key group g: byte 16*(b%2) + r holds accumulator element
-    // r of key block b = 2g + b%2.
-    auto softmax = [&](int j, f32x16 (&s)[NB], i32x8 (&pf)[NG], bool masked) __attribute__((always_inline)) {
-        if (masked) {
-            const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+        // ---- HBM -> LDS, 16 bytes per lane; wave-load n of this wave fills LDS
+        // chunks [64*(wave + WAVES*n), +64).  Past-the-end rows read as zero.
+        uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
+        for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
+            const int c = (wave + WAVES * n) * 64 + lane;
+            k_off[n] = L::k_src(c);
+            v_off[n] = L::v_src(c);
+        }
+        auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(tile * BC * D);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    if (kk > lim) s[b][r] = -INFINITY;
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                if (T::LOADS % WAVES == 0 || wave + WAVES * n < T::LOADS)
+                    buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 1024);
+        };
+        auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = (uint32_t)(tile * BC * D);
+#pragma unroll
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                if (T::LOADS % WAVES == 0 || wave + WAVES * n < T::LOADS)
+                    buf_load16_lds(rv, base + v_off[n], Vbuf + buf * T::TILE + (wave + WAVES * n) * 1024);
+        };
+
+        auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
+            const uint8_t *Ks = Kbuf + buf * T::TILE;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < D / 64; ++st) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const u32x4 w[2] = {lds_read16(Ks + L::k_read(st, b, 0, lane)),
+                                        lds_read16(Ks + L::k_read(st, b, 1, lane))};
+                    s[b] = mfma_f8(__builtin_bit_cast(i32x8, w), qf[st], s[b]);
                 }
             }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-        mx = pair_max(mx) * c;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_safe);
-            m_run = m_safe;
-            l_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-        }
-        float rs0, rs1;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
-                const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
-                const float p2 = fast_exp2(fmaf(s[b][r + 2], c, -m_run));
-                const float p3 = fast_exp2(fmaf(s[b][r + 3], c, -m_run));
-                if (b == 0 && r == 0) {
-                    rs0 = p0 + p2;
-                    rs1 = p1 + p3;
-                } else {
-                    rs0 += p0 + p2;
-                    rs1 += p1 + p3;
-                }
-                const int slot = 4 * (b & 1) + (r >> 2);
-                pf[b >> 1][slot] = pack_e4m3x4(p0, p1, p2, p3, pf[b >> 1][slot]);
-            }
-        }
-        l_run += rs0 + rs1;
-    };
-    // O^T += V_tile^T P^T, one 64-key contraction per head-dim block.
-    auto pv = [&](int buf, const i32x8 (&pf)[NG]) __attribute__((always_inline)) {
-        const uint8_t *Vs = Vbuf + buf * T::TILE;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) {
-                const uint8_t *Vg = Vs + 64 * g * D;
-                const i32x2 w[4] = {lds_read_tr8(Vg + L::v_read(0, t, lane)), lds_read_tr8(Vg + L::v_read(1, t, lane)),
-                                    lds_read_tr8(Vg + L::v_read(2, t, lane)), lds_read_tr8(Vg + L::v_read(3, t, lane))};
-                acc[t] = mfma_f8(__builtin_bit_cast(i32x8, w), pf[g], acc[t]);
-            }
-        }
-    };
+        };
+        auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
 
-    i32x8 pf[NG];
+        const float c = p.scale_log2;
+        float m_run = -INFINITY;
+        float l_run = 0.f;
+        f32x16 acc[D / 32];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) pf[g] = i32x8{};
-    // Double-buffered tiles: tile j+1 streams into LDS while tile j is used.
-    load_k(0, 0);
-    load_v(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles) {
-            load_k(j + 1, buf ^ 1);
-            load_v(j + 1, buf ^ 1);
-        }
-        if (active(j)) {
-            f32x16 s[NB];
-            scores(buf, s);
-            softmax(j, s, pf, j >= nfull);
-            pv(buf, pf);
-        }
+        for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+        // Online softmax of score tile j.  pf[g] is the e4m3 B operand of the P*V
+        // product for 64-key group g: byte 16*(b%2) + r holds accumulator element
+        // r of key block b = 2g + b%2.
+        auto softmax = [&](int j, f32x16 (&s)[NB], i32x8 (&pf)[NG], bool masked) __attribute__((always_inline)) {
+            if (masked) {
+                const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (kk > lim) s[b][r] = -INFINITY;
+                    }
+                }
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+            mx = pair_max(mx) * c;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_safe);
+                m_run = m_safe;
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+            }
+            float rs0, rs1;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
+                    const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
+                    const float p2 = fast_exp2(fmaf(s[b][r + 2], c, -m_run));
+                    const float p3 = fast_exp2(fmaf(s[b][r + 3], c, -m_run));
+                    if (b == 0 && r == 0) {
+                        rs0 = p0 + p2;
+                        rs1 = p1 + p3;
+                    } else {
+                        rs0 += p0 + p2;
+                        rs1 += p1 + p3;
+                    }
+                    const int slot = 4 * (b & 1) + (r >> 2);
+                    pf[b >> 1][slot] = pack_e4m3x4(p0, p1, p2, p3, pf[b >> 1][slot]);
+                }
+            }
+            l_run += rs0 + rs1;
+        };
+        // O^T += V_tile^T P^T, one 64-key contraction per head-dim block.
+        auto pv = [&](int buf, const i32x8 (&pf)[NG]) __attribute__((always_inline)) {
+            const uint8_t *Vs = Vbuf + buf * T::TILE;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) {
+                    const uint8_t *Vg = Vs + 64 * g * D;
+                    const i32x2 w[4] = {lds_read_tr8(Vg + L::v_read(0, t, lane)),
+                                        lds_read_tr8(Vg + L::v_read(1, t, lane)),
+                                        lds_read_tr8(Vg + L::v_read(2, t, lane)),
+                                        lds_read_tr8(Vg + L::v_read(3, t, lane))};
+                    acc[t] = mfma_f8(__builtin_bit_cast(i32x8, w), pf[g], acc[t]);
+                }
+            }
+        };
+
+        i32x8 pf[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) pf[g] = i32x8{};
+        // Double-buffered tiles: tile j+1 streams into LDS while tile j is used.
+        load_k(0, 0);
+        load_v(0, 0);
         wait_vmem();
         __syncthreads();
-    }
-
-    const float l_tot = pair_sum(l_run);
-    const float inv = p.v_descale / l_tot;
-    if (qrow < N) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
-                buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+        for (int j = 0; j < ntiles; ++j) {
+            const int buf = j & 1;
+            if (j + 1 < ntiles) {
+                load_k(j + 1, buf ^ 1);
+                load_v(j + 1, buf ^ 1);
             }
+            if (active(j)) {
+                f32x16 s[NB];
+                scores(buf, s);
+                softmax(j, s, pf, j >= nfull);
+                pv(buf, pf);
+            }
+            wait_vmem();
+            __syncthreads();
         }
-        if (hf == 0 && p.lse) p.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+
+        const float l_tot = pair_sum(l_run);
+        const float inv = p.v_descale / l_tot;
+        if (qrow < N) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+                    w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+                    buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+                }
+            }
+            if (hf == 0 && p.lse) p.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
     }
 }
 
@@ -350,7 +360,8 @@ hipError_t launch(const Fp8Args &a, hipStream_t s) {
     p.nqb = (a.f.N + T::BR - 1) / T::BR;
     p.scale_log2 = a.f.scale * a.q_descale * a.k_descale * kLog2e;
     p.v_descale = a.v_descale;
-    const unsigned blocks = (unsigned)a.f.BH * (unsigned)p.nqb;
+    p.paired = CAUSAL && pair_causal_blocks((long long)a.f.BH * p.nqb, WAVES == 8 ? 1 : 2);
+    const unsigned blocks = (unsigned)a.f.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
     hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }

@@ -106,6 +106,24 @@ def test_backward_sampled(ea, W, oracle_mod, name, nslices, nsamp):
     check(got, ref, name)
 
 
+def test_backward_causal_paired_odd_block_count(ea, W, oracle_mod):
+    # B*H*ceil(N/128) >= 1024 pairs the causal key blocks (dK, dV) and query
+    # blocks (dQ); N = 17 * 128 leaves one workgroup per slice with the middle
+    # block alone.  Rows and keys are taken from the first, middle and last
+    # blocks and from block boundaries.
+    B, H, N, d = 1, 64, 17 * 128, 128
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=91)
+    g = W.make_grad(B, H, N, d, torch.bfloat16, seed=91)
+    say(f"[bwd] causal B={B} H={H} N={N} (17 blocks of 128)")
+    dq, dk, dv = gpu_grads(ea, q, k, v, g, True)
+    idx = [0, 1, 127, 128, 1023, 1024, 1100, 1151, 1152, 2047, 2048, N - 1]
+    slices = [0, B * H - 1]
+    flat = lambda t: t.reshape(-1, N, d)[slices]  # noqa: E731
+    ref = oracle_mod.attention_backward(flat(q), flat(k), flat(v), flat(g), 1 / math.sqrt(d), True,
+                                        rows=idx, keys=idx)
+    check((flat(dq)[:, idx], flat(dk)[:, idx], flat(dv)[:, idx]), ref, "paired, 17 blocks")
+
+
 def test_backward_closed_forms_and_determinism(ea, W):
     q, k, v = (t.cuda() for t in W.make_qkv(2, 4, 700, 128, torch.bfloat16, seed=31))
     g = W.make_grad(2, 4, 700, 128, torch.bfloat16, seed=31).cuda()

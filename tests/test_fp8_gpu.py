@@ -121,6 +121,12 @@ def test_dense_8k(ea, W, oracle_mod):
     _sliced(ea, W, oracle_mod, 8, 32, 8192, 128, False, 1.0, 2, 64, "dense 8k")
 
 
+def test_causal_paired_odd_block_count(ea, W, oracle_mod):
+    # B*H*ceil(N/128) >= 1024 pairs causal query blocks; N = 17 * 128 leaves
+    # one workgroup per slice with the middle block alone.  All rows checked.
+    _sliced(ea, W, oracle_mod, 1, 64, 17 * 128, 128, True, 1.0, 2, 17 * 128, "causal paired, 17 blocks")
+
+
 def test_causal_32k_qx8(ea, W, oracle_mod):
     _sliced(ea, W, oracle_mod, 1, 32, 32768, 128, True, 8.0, 2, 32, "causal 32k Qx8")
 
