@@ -5,9 +5,13 @@ Test infrastructure, not product code: only ``tests/``,
 it.  The HIP library neither imports nor links anything here, and this package
 imports nothing from the HIP library.
 
-The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, the textbook
-definition: scores, row max, exp-sum, weighted values).  This module only
-builds that file with gcc and marshals numpy arrays through ctypes.
+The attention arithmetic lives in plain C, fp64: ``attn_oracle.c`` (the
+textbook forward: scores, row max, exp-sum, weighted values),
+``attn_bwd_oracle.c`` (its gradients), ``attn_probs_oracle.c`` (rows of the
+probability matrix) and ``attn_masked_oracle.c`` (forward with window masks
+and an additive bias).  This module builds them with gcc and marshals numpy
+arrays through ctypes; the e4m3 decoding and the elementwise chain
+(relu(scale * x + bias)) are written out here in numpy.
 
 Definition followed: grasp.study lesson on standard self-attention, section
 "The Computational Steps of Standard Self-Attention" (scores = Q K^T, row-wise
