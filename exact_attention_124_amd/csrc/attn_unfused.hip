@@ -242,32 +242,10 @@ __global__ __launch_bounds__(256) void softmax_rows_bf16_stream_kernel(uint16_t 
 // is multiplied.  P is the one N x N read of this launch, and a tile fetched
 // only one ahead leaves each iteration waiting a full memory latency.
 //
-// The direct-to-LDS loads are issued from inline assembly: the compiler counts
-// its own such loads as writes to all of LDS that every workgroup barrier (a
-// release fence) and every LDS read must wait for, which would drain the whole
-// ring each iteration.  Completion is tracked here instead: a wave waits until
-// at most the loads of the newer tiles are outstanding (vector-memory loads
-// complete in order) and then meets the barrier.  M0, which holds the LDS
-// destination, is saved and restored around each load.
+// The direct-to-LDS loads are load16_lds_async (inline assembly, see
+// common.h): a wave waits until at most the loads of the newer tiles are
+// outstanding and then meets the barrier.
 // ---------------------------------------------------------------------------
-template <int N_>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N_ >= 0 && N_ < 64, "vmcnt is a 6-bit field");
-    __builtin_amdgcn_s_waitcnt((N_ & 15) | (((N_ >> 4) & 3) << 14) | 0x0F70);
-}
-__device__ __forceinline__ void load16_lds_async(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void *lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(base), "v"(voff), "s"(r)
-        : "memory");
-}
 
 template <int D>
 __global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,

@@ -79,6 +79,35 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Wait until at most N_ vector-memory operations of this wave are outstanding.
+// Loads complete in issue order, so this means every load older than the
+// newest N_ has landed.
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | (((N_ >> 4) & 3) << 14) | 0x0F70);
+}
+
+// buf_load16_lds issued from inline assembly, for kernels that keep several
+// tiles in flight.  The compiler counts its own direct-to-LDS loads as writes
+// to all of LDS that every barrier (a release fence) and every LDS read must
+// wait for, which would drain all of them at each tile; hidden from it, the
+// caller tracks completion with wait_vmcnt.  M0, which holds the LDS
+// destination, is saved and restored around the load.
+__device__ __forceinline__ void load16_lds_async(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r)
+        : "memory");
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats -> two bf16 (round to nearest even) packed low/high in one word.

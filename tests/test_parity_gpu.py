@@ -219,6 +219,22 @@ def test_edge_shapes_bf16(ea, W, oracle_mod, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_edge_shapes_many_slices_bf16(ea, W, oracle_mod, d, causal):
+    # With few (batch, head) slices the forward runs the split-key kernel (the
+    # shapes above); 130 slices make every N here launch more than 128 blocks
+    # of 128 rows, so the regular kernel handles the same ragged lengths.
+    slices = [0, 64, 129]
+    for N in [17, 129, 200, 1000]:
+        q, k, v = W.make_qkv(1, 130, N, d, torch.bfloat16, seed=500 + N)
+        qs, ks, vs = (t.reshape(-1, N, d)[slices] for t in (q, k, v))
+        ro, rl = oracle_mod.attention(qs, ks, vs, 1 / math.sqrt(d), causal)
+        say(f"[edge] bf16 130 slices N={N} d={d} causal={causal}")
+        o, lse = run(ea, q, k, v, causal)
+        check_bf16(o.reshape(-1, N, d)[slices], lse.reshape(-1, N)[slices], ro, rl, "fused, regular kernel")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 def test_edge_shapes_f32(ea, W, oracle_mod, d, causal):
     for N in [1, 5, 31, 32, 33, 127, 129, 300]:
         q, k, v = W.make_qkv(1, 2, N, d, torch.float32, seed=100 + N)
@@ -320,19 +336,29 @@ def test_rejects_bad_head_dim_on_device(ea):
 
 def test_schedule_independence(ea, W):
     # The same slice computed inside a large batch (eight-wave workgroups,
-    # K-ahead pipeline) and alone (four-wave workgroups, plain loop) visits
-    # the same key tiles in the same order for every row, with the same
-    # 32-row wave, so the results must agree bit for bit.
-    for B, H, N, causal in ((4, 64, 1024, False), (1, 32, 8192, True)):
+    # K-ahead pipeline) and in a batch of copies of it small enough for
+    # four-wave workgroups (plain loop) visits the same key tiles in the same
+    # order for every row, with the same 32-row wave, so the results must agree
+    # bit for bit.  Alone, the slice takes the split-key kernel, which sums the
+    # keys in another order: it must agree within the bf16 tolerance.
+    for B, H, N, causal, copies in ((4, 64, 1024, False, 32), (1, 32, 8192, True, 8)):
         q, k, v = (t.cuda() for t in W.make_qkv(B, H, N, 128, torch.bfloat16, seed=21))
         say(f"[schedule] B={B} H={H} N={N} causal={causal}")
         o_all, l_all = ea.attention(q, k, v, causal=causal)
         for idx in (0, B * H - 1):
             b, h = divmod(idx, H)
             qs, ks, vs = (t[b:b + 1, h:h + 1].contiguous() for t in (q, k, v))
+            qc, kc, vc = (t.expand(1, copies, N, 128).contiguous() for t in (qs, ks, vs))
+            oc, lc = ea.attention(qc, kc, vc, causal=causal)
             o1, l1 = ea.attention(qs, ks, vs, causal=causal)
             torch.cuda.synchronize()
-            assert torch.equal(o1[0, 0], o_all[b, h]), (B, H, N, causal, idx)
-            assert torch.equal(l1[0, 0], l_all[b, h]), (B, H, N, causal, idx)
+            for c in (0, copies - 1):
+                assert torch.equal(oc[0, c], o_all[b, h]), (B, H, N, causal, idx, c)
+                assert torch.equal(lc[0, c], l_all[b, h]), (B, H, N, causal, idx, c)
+            d_o = (o1[0, 0].float() - o_all[b, h].float()).abs()
+            d_l = (l1[0, 0] - l_all[b, h]).abs().max().item()
+            say(f"  split-key vs regular: max|dO|={d_o.max().item():.3e} mean={d_o.mean().item():.3e} "
+                f"max|dlse|={d_l:.3e}")
+            assert d_o.max().item() <= BF16_MAX and d_o.mean().item() <= BF16_MEAN and d_l <= BF16_LSE
         del q, k, v, o_all, l_all
         torch.cuda.empty_cache()
