@@ -599,7 +599,9 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     if (blocks4 <= 128) return launch_split<D, CAUSAL>(a, s);
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
     const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.N <= 4096);
-    return wide ? launch<D, CAUSAL, 8, 64, true>(a, s) : launch<D, CAUSAL, 4, 64, false>(a, s);
+    if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
+    if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
+    else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {

@@ -25,6 +25,8 @@ struct FwdArgs {
 
 // Fused forward (one kernel launch).
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
+// Non-causal 8-wave forward (attn_fwd_bf16_dense.hip); called by launch_fwd_bf16.
+hipError_t launch_fwd_bf16_dense8(const FwdArgs &a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 
 // Fused forward on OCP e4m3 inputs with per-tensor dequantisation factors;
