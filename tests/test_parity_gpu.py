@@ -246,6 +246,37 @@ def test_edge_shapes_f32(ea, W, oracle_mod, d, causal):
         check_f32(o, lse, ro, rl, "unfused")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_shapes_many_slices_f32(ea, W, oracle_mod, d, causal):
+    # Grids of fewer workgroups than compute units (the shapes above) run the
+    # split-key fp32 kernel; 260 slices launch at least 260 blocks of 128
+    # rows, so the regular kernel sees the same ragged lengths.
+    slices = [0, 129, 259]
+    for N in [17, 129, 300]:
+        q, k, v = W.make_qkv(1, 260, N, d, torch.float32, seed=700 + N)
+        qs, ks, vs = (t.reshape(-1, N, d)[slices] for t in (q, k, v))
+        ro, rl = oracle_mod.attention(qs, ks, vs, 1 / math.sqrt(d), causal)
+        say(f"[edge] fp32 260 slices N={N} d={d} causal={causal}")
+        o, lse = run(ea, q, k, v, causal)
+        check_f32(o.reshape(-1, N, d)[slices], lse.reshape(-1, N)[slices], ro, rl,
+                  "fused, regular kernel")
+
+
+def test_large_logits_f32(ea, W, oracle_mod):
+    # Q x 8 through both fp32 kernels: the split one (2 slices) and the
+    # regular one (256 slices, three of them checked).
+    for causal in (False, True):
+        for H, slices in ((2, [0, 1]), (256, [3, 100, 255])):
+            q, k, v = W.make_qkv(1, H, 300, 64, torch.float32, seed=31, q_mult=8.0)
+            qs, ks, vs = (t.reshape(-1, 300, 64)[slices] for t in (q, k, v))
+            ro, rl = oracle_mod.attention(qs, ks, vs, 1 / 8.0, causal)
+            say(f"[edge] fp32 Qx8 H={H} N=300 causal={causal}")
+            o, lse = run(ea, q, k, v, causal)
+            check_f32(o.reshape(-1, 300, 64)[slices], lse.reshape(-1, 300)[slices], ro, rl,
+                      f"fused H={H}")
+
+
 def test_large_logits_bf16(ea, W, oracle_mod):
     # Q x 8 at a small size: frequent running-max rescales.
     for causal in (False, True):
