@@ -38,6 +38,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace fwd_bf16 {
 
@@ -266,12 +268,20 @@ void kernel(Params p) {
             l_run += rs0 + rs1;
         };
         // O^T += V_tile^T P^T.
+        // The V^T operands are read two products ahead, so each transpose read
+        // has two MFMAs' time to return (one read in flight left the LDS
+        // latency exposed before every product).
         auto pv = [&](int buf, const bf16x8 (&pb)[2 * NB]) __attribute__((always_inline)) {
             const uint16_t *Vs = Vbuf + buf * T::TILE;
+            constexpr int TB = D / 32, NOPS = (BC / 16) * TB, DEPTH = 3;
+            bf16x8 vo[DEPTH];
 #pragma unroll
-            for (int st = 0; st < BC / 16; ++st) {
+            for (int i = 0; i < DEPTH - 1; ++i) vo[i] = v_operand(Vs, i / TB, i % TB);
 #pragma unroll
-                for (int t = 0; t < D / 32; ++t) acc[t] = mfma32(v_operand(Vs, st, t), pb[st], acc[t]);
+            for (int i = 0; i < NOPS; ++i) {
+                const int nx = i + DEPTH - 1;
+                if (nx < NOPS) vo[nx % DEPTH] = v_operand(Vs, nx / TB, nx % TB);
+                acc[i % TB] = mfma32(vo[i % DEPTH], pb[i / TB], acc[i % TB]);
             }
         };
 
@@ -288,26 +298,35 @@ void kernel(Params p) {
             // The first step refills K buffer 0 (tile 2); every wave must have
             // finished reading tile 0 from it first.
             __syncthreads();
-            auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
+            // CHECKED is false for steps whose tiles j and j+1 are both below
+            // nfull: every wave visits them and no key needs a mask, so the
+            // main loop carries no per-tile tests; the remaining steps (the
+            // diagonal of a causal block, a ragged last tile) run checked.
+            auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB], auto checked) __attribute__((always_inline)) {
+                constexpr bool CHECKED = decltype(checked)::value;
                 if (j + 2 < ntiles) load_k(j + 2, j & 1);
-                if (j + 1 < ntiles) {
+                if (!CHECKED || j + 1 < ntiles) {
                     load_v(j + 1, (j + 1) & 1);
-                    if (active(j + 1)) scores((j + 1) & 1, nxt);
+                    if (!CHECKED || active(j + 1)) scores((j + 1) & 1, nxt);
                 }
-                if (active(j)) {
+                if (!CHECKED || active(j)) {
                     bf16x8 pb[2 * NB];
-                    softmax(j, cur, pb, j >= nfull);
+                    softmax(j, cur, pb, CHECKED && j >= nfull);
                     pv(j & 1, pb);
                 }
                 wait_vmem();
                 __syncthreads();
             };
             int j = 0;
-            for (; j + 1 < ntiles; j += 2) {
-                step(j, sa, sb);
-                step(j + 1, sb, sa);
+            for (; j + 2 < nfull; j += 2) {
+                step(j, sa, sb, std::false_type{});
+                step(j + 1, sb, sa, std::false_type{});
             }
-            if (j < ntiles) step(j, sa, sb);
+            for (; j + 1 < ntiles; j += 2) {
+                step(j, sa, sb, std::true_type{});
+                step(j + 1, sb, sa, std::true_type{});
+            }
+            if (j < ntiles) step(j, sa, sb, std::true_type{});
         } else {
             load_k(0, 0);
             load_v(0, 0);
