@@ -185,6 +185,29 @@ def test_causal_odd_block_count_eight_waves(ea, W, oracle_mod):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_eight_wave_ragged(ea, W, oracle_mod, d, causal):
+    # Grids of at least 1024 256-row blocks (and, causal, N > 4096) select the
+    # 8-wave K-ahead kernels; N = 1000 and 4100 end in a partial 64-key tile,
+    # so the last steps take the checked path (masked tail keys, and for
+    # causal the diagonal), after the unchecked main loop.  Rows come from
+    # the first block, tile and block boundaries and the ragged end.
+    N = 4100 if causal else 1000
+    B, H = (1, 64) if causal else (4, 64)
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=900 + d + causal)
+    rows = sorted({0, 1, 63, 64, 255, 256, N // 2, N - 66, N - 65, N - 64, N - 5, N - 1})
+    slices = [0, 37, B * H - 1]
+    say(f"[parity] 8-wave ragged B={B} H={H} N={N} d={d} causal={causal}")
+    qs, ks, vs = (t.reshape(-1, N, d)[slices] for t in (q, k, v))
+    ro, rl = oracle_mod.attention(qs, ks, vs, 1 / math.sqrt(d), causal, rows=rows)
+    o, lse = ea.attention(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    sl, rw = torch.tensor(slices, device=o.device), torch.tensor(rows, device=o.device)
+    check_bf16(o.reshape(-1, N, d)[sl][:, rw], lse.reshape(-1, N)[sl][:, rw], ro, rl, "fused 8-wave, ragged N")
+    assert torch.isfinite(o).all().item()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 def test_unfused_ring_shapes(ea, W, oracle_mod, d, causal):
     # N a multiple of 8 takes the LDS-ring P*V kernel (256 query rows per
     # workgroup, 64-key tiles): one tile, one exact block, ragged rows and keys
