@@ -606,8 +606,9 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
 // 8 waves (256 query rows) per workgroup share each K/V tile and run the
 // K-ahead pipeline.  4 waves (128 rows, two workgroups per CU, plain loop)
 // are used when 8-wave workgroups would leave fewer than four per CU, and for
-// causal sequences up to 4096, where the waves of a 256-row block differ by up
-// to 3.5 tiles of causal work and the shorter block wastes less of it.  When
+// causal sequences up to 1024, where the waves of a 256-row block differ by up
+// to 3.5 tiles of causal work and the shorter block wastes more of the whole.
+// (From 1280 to 4096 keys, causal, the 8-wave kernel measured 1-7 % faster.)  When
 // even the 4-wave grid has at most 128 workgroups (half a workgroup per CU),
 // the split-key kernel runs instead: four times the workgroups, each wave a
 // quarter of the keys (measured 8-37 % faster there, 40 % slower at 256).
@@ -617,7 +618,7 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const long long blocks4 = (long long)a.BH * ((a.N + 127) / 128);
     if (blocks4 <= 128) return launch_split<D, CAUSAL>(a, s);
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
-    const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.N <= 4096);
+    const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.N <= 1024);
     if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
     if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
     else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
