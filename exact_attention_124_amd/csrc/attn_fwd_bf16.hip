@@ -605,10 +605,12 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
 #ifndef ATTN_FWD_BF16_NO_DEFAULT_LAUNCHER
 // 8 waves (256 query rows) per workgroup share each K/V tile and run the
 // K-ahead pipeline.  4 waves (128 rows, two workgroups per CU, plain loop)
-// are used when 8-wave workgroups would leave fewer than four per CU, and for
-// causal sequences up to 1024, where the waves of a 256-row block differ by up
-// to 3.5 tiles of causal work and the shorter block wastes more of the whole.
-// (From 1280 to 4096 keys, causal, the 8-wave kernel measured 1-7 % faster.)  When
+// are used when there would be fewer than 192 8-wave workgroups (three
+// quarters of one per CU: at 128 the 8-wave grid leaves half the CUs idle and
+// measured 11-13 % slower, at 192 and above it measured up to 15 % faster),
+// and for causal sequences up to 1024 keys, where the waves of a 256-row block
+// differ by up to 3.5 tiles of causal work and the shorter block wastes more
+// of the whole.  When
 // even the 4-wave grid has at most 128 workgroups (half a workgroup per CU),
 // the split-key kernel runs instead: four times the workgroups, each wave a
 // quarter of the keys (measured 8-37 % faster there, 40 % slower at 256).
@@ -618,7 +620,7 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const long long blocks4 = (long long)a.BH * ((a.N + 127) / 128);
     if (blocks4 <= 128) return launch_split<D, CAUSAL>(a, s);
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
-    const bool wide = blocks8 >= 4 * 256 && !(CAUSAL && a.N <= 1024);
+    const bool wide = blocks8 >= 192 && !(CAUSAL && a.N <= 1024);
     if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
     if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
     else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
