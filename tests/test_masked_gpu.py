@@ -128,14 +128,13 @@ def test_causal_32k_sliding_window(ea, W, oracle_mod):
     _sampled(ea, W, oracle_mod, 1, 32, 32768, 128, True, 8.0, (4096, -1), None, 32, "causal 32k Qx8, window 4096")
 
 
-def test_grouped_bias_mapping(ea, W, oracle_mod):
-    # A bias broadcast over the batch on a grid of at least 4096 workgroups
-    # runs workgroups in groups of 8 slices (one head, 8 batch entries) x 8
-    # query blocks.  Every output element must be written exactly by its own
-    # workgroup: outputs start as NaN, and sampled rows of slices spread over
-    # batch and heads are checked against the oracle with their head's bias.
+def test_per_head_bias_large_grid(ea, W, oracle_mod):
+    # A bias broadcast over the batch (stride 0) but not over heads, on a grid
+    # of 4096 workgroups: every output element must be written (outputs start
+    # as NaN), and sampled rows of slices spread over batch and heads must
+    # match the oracle with their own head's bias.
     B, H, N, d = 8, 16, 4096, 128
-    say(f"[masked] grouped bias mapping B={B} H={H} N={N}, per-head bias")
+    say(f"[masked] per-head bias B={B} H={H} N={N}")
     q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=5)
     bias = W.make_bias(1, H, N, seed=6, scale=2.0, drop=0.05)
     qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
@@ -149,4 +148,4 @@ def test_grouped_bias_mapping(ea, W, oracle_mod):
     for b, h in [(0, 0), (7, 15), (3, 5), (5, 3), (1, 14), (6, 9), (2, 0), (4, 11), (0, 15), (7, 0), (3, 8), (6, 1)]:
         ro, rl = oracle_mod.attention_masked(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
                                              1 / math.sqrt(d), False, -1, -1, bias[:, h:h + 1], rows=rows)
-        check(o[b:b + 1, h:h + 1, r].cpu(), lse[b:b + 1, h:h + 1, r].cpu(), ro, rl, f"grouped bias b={b} h={h}")
+        check(o[b:b + 1, h:h + 1, r].cpu(), lse[b:b + 1, h:h + 1, r].cpu(), ro, rl, f"per-head bias b={b} h={h}")
