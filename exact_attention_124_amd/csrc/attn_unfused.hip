@@ -92,7 +92,10 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t *__rest
         uint16_t *dst = S + ((size_t)bh * N + i) * N + j;
         const uint16_t *src = smem + row * SSTR + col;
         if (VEC) {
-            *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+            // S streams through (34 GB at the dense 8k shape, far beyond L2 and
+            // MALL): non-temporal stores measured 6 % faster for this kernel.
+            // (The same on the softmax's in-place accesses was 8 % slower.)
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst));
         } else {
             for (int e = 0; e < 8 && j + e < N; ++e) dst[e] = src[e];
         }
