@@ -31,6 +31,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace fwd_fp8 {
 
@@ -313,21 +315,31 @@ void kernel(Params p) {
         load_v(0, 0);
         wait_vmem();
         __syncthreads();
-        for (int j = 0; j < ntiles; ++j) {
+        // Causal: tiles below nfull are visited by every wave and need no
+        // mask, so they run in a loop without the per-tile tests; the rest
+        // (the diagonal, a ragged last tile) run checked.
+        auto step = [&](int j, auto checked) __attribute__((always_inline)) {
+            constexpr bool CHECKED = decltype(checked)::value;
             const int buf = j & 1;
-            if (j + 1 < ntiles) {
+            if (!CHECKED || j + 1 < ntiles) {
                 load_k(j + 1, buf ^ 1);
                 load_v(j + 1, buf ^ 1);
             }
-            if (active(j)) {
+            if (!CHECKED || active(j)) {
                 f32x16 s[NB];
                 scores(buf, s);
-                softmax(j, s, pf, j >= nfull);
+                softmax(j, s, pf, CHECKED && j >= nfull);
                 pv(buf, pf);
             }
             wait_vmem();
             __syncthreads();
-        }
+        };
+        // (Causal only: on the dense 8k shape the split loop measured 2 %
+        // slower than one checked loop, on causal 32k 4.7 % faster.)
+        int j = 0;
+        if constexpr (CAUSAL)
+            for (; j + 1 < nfull; ++j) step(j, std::false_type{});
+        for (; j < ntiles; ++j) step(j, std::true_type{});
 
         const float l_tot = pair_sum(l_run);
         const float inv = p.v_descale / l_tot;
