@@ -369,24 +369,32 @@ void kernel(Params p) {
     }
 }
 
-// Small grids (fewer query blocks than CUs): the four waves of a workgroup
-// share one 32-row query block and split its keys, wave w taking key tiles
-// w, w+4, w+8, ...  Each wave streams its tiles through its own double-buffered
-// LDS slots, so the loop has no workgroup barrier.  The per-wave online
-// softmax is the one above, with one 32-key block per tile.  At the end every
-// wave leaves (m, l, O accumulator) in LDS, and wave t combines head-dim block
-// t of the four partials:
+// Small grids (fewer query blocks than CUs): the SW waves of a workgroup
+// share one block of 32*RB query rows and split its keys, wave w taking key
+// tiles w, w+SW, w+2*SW, ...  Each wave streams its tiles through its own
+// double-buffered LDS slots, so the loop has no workgroup barrier.  With RB = 2
+// a wave computes two 32-row blocks from every K and V operand it reads.  The
+// per-wave online softmax is the one above, with one 32-key block per tile.
+// At the end every wave leaves (m, l, O accumulator) per row block in LDS, and
+// one wave per (row block, head-dim block) pair combines the SW partials:
 //     m = max_w m_w,   l = sum_w 2^(m_w - m) l_w,   O = sum_w 2^(m_w - m) O_w / l
 // (the merge of online-softmax states over disjoint key sets).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void split_kernel(Params p) {
+// Shapes: 4 waves x 32 rows, and (non-causal, d = 64) 8 waves x 64 rows, which
+// halves the tiles each wave walks one after another and the grid.
+template <int D, bool CAUSAL, int SW, int RB>
+__global__ __launch_bounds__(64 * SW) void split_kernel(Params p) {
     using L = Layout<D>;
     constexpr int BC = 32;                  // keys per tile
     constexpr int TILE = BC * D;            // elements per K or V tile
     constexpr int LPT = TILE * 2 / 1024;    // 1 KiB loads per K (or V) tile
     constexpr int WREG = 4 * TILE;          // per-wave LDS elements: K[2], V[2]
-    static_assert(32 * D + 128 <= 2 * TILE, "the partials must fit a wave's LDS slots");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * WREG];
+    constexpr int TB = D / 32;              // head-dim blocks
+    static_assert(RB * 32 * D <= 2 * TILE, "the partial accumulators must fit a wave's LDS slots");
+    static_assert(RB * TB <= SW, "one merging wave per (row block, head-dim block)");
+    static_assert(!CAUSAL || RB == 1, "a causal row block must see an allowed key in every visited tile");
+    // SW waves x (K[2], V[2]) slots, then each wave's (m, l) per row block.
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SW * WREG + SW * RB * 128 * 2];
+    float *const ml = reinterpret_cast<float *>(smem + SW * WREG);  // [SW][RB][2][64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -405,13 +413,15 @@ __global__ __launch_bounds__(256) void split_kernel(Params p) {
     const auto rk = make_rsrc(p.k + slice, slice_bytes);
     const auto rv = make_rsrc(p.v + slice, slice_bytes);
     const auto ro = make_rsrc(p.o + slice, slice_bytes);
-    const int r0 = qb * 32;
-    const int qrow = r0 + l32;
+    const int r0 = qb * 32 * RB;
 
-    bf16x8 qf[D / 16];
+    bf16x8 qf[RB][D / 16];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            qf[rb][s] = __builtin_bit_cast(
+                bf16x8, buf_load16(rq, (uint32_t)((r0 + 32 * rb + l32) * D + 16 * s + 8 * hf) * 2u));
 
     int ntiles = (N + BC - 1) / BC;
     int nfull = N / BC;
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(256) void split_kernel(Params p) {
         ntiles = min(ntiles, (r0 + 31) / BC + 1);
         nfull = min(nfull, (r0 + 1) / BC);
     }
-    const int mine = ntiles > wave ? (ntiles - 1 - wave) / 4 + 1 : 0;  // tiles of this wave
+    const int mine = ntiles > wave ? (ntiles - 1 - wave) / SW + 1 : 0;  // tiles of this wave
 
     uint32_t k_off[LPT], v_off[LPT];
 #pragma unroll
@@ -436,111 +446,128 @@ __global__ __launch_bounds__(256) void split_kernel(Params p) {
     };
 
     const float c = p.scale_log2;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x16 acc[D / 32];
+    float m_run[RB], l_run[RB];
+    f32x16 acc[RB][TB];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[rb][t] = f32x16{};
+    }
 
     if (mine > 0) load(wave, 0);
     for (int i = 0; i < mine; ++i) {
-        const int j = wave + 4 * i;
+        const int j = wave + SW * i;
         // Tile j has landed once at most the next tile's loads are pending.
         // The slot refilled here was last read in iteration i-1 by this wave,
         // whose reads were consumed (and so completed) before it got here.
         // (Three or four slots per wave were slower: the workgroup's LDS then
         // allows one workgroup per CU.)
         if (i + 1 < mine) {
-            load(j + 4, (i + 1) & 1);
+            load(j + SW, (i + 1) & 1);
             wait_vmcnt<2 * LPT>();
         } else {
             wait_vmcnt<0>();
         }
         const uint16_t *Ks = Kw + (i & 1) * TILE;
         const uint16_t *Vs = Vw + (i & 1) * TILE;
-        f32x16 sc = f32x16{};
+        f32x16 sc[RB];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-            sc = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, 0, lane)), qf[st], sc);
-        if (j >= nfull) {  // keys past the end of the sequence and, if causal, past the query
-            const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+        for (int rb = 0; rb < RB; ++rb) sc[rb] = f32x16{};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = j * BC + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (kk > lim) sc[r] = -INFINITY;
+        for (int st = 0; st < D / 16; ++st) {
+            const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, 0, lane));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) sc[rb] = mfma32(kop, qf[rb][st], sc[rb]);
+        }
+        bf16x8 pb[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            if (j >= nfull) {  // keys past the end of the sequence and, if causal, past the query
+                const int lim = CAUSAL ? min(r0 + 32 * rb + l32, N - 1) : N - 1;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = j * BC + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (kk > lim) sc[rb][r] = -INFINITY;
+                }
             }
-        }
-        float mx = sc[0];
+            float mx = sc[rb][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-        mx = pair_max(mx) * c;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_safe);
-            m_run = m_safe;
-            l_run *= alpha;
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[rb][r]);
+            mx = pair_max(mx) * c;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run[rb] + kLazyThreshold) != 0) {
+                const float m_new = fmaxf(m_run[rb], mx);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run[rb] - m_safe);
+                m_run[rb] = m_safe;
+                l_run[rb] *= alpha;
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-        }
-        bf16x8 pb[2];
-        float rs0 = 0.f, rs1 = 0.f;
+                for (int t = 0; t < TB; ++t) acc[rb][t] *= alpha;
+            }
+            float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(sc[r], c, -m_run));
-            const float p1 = fast_exp2(fmaf(sc[r + 1], c, -m_run));
-            rs0 += p0;
-            rs1 += p1;
-            pb[r >> 3][r & 7] = (__bf16)p0;
-            pb[r >> 3][(r & 7) + 1] = (__bf16)p1;
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sc[rb][r], c, -m_run[rb]));
+                const float p1 = fast_exp2(fmaf(sc[rb][r + 1], c, -m_run[rb]));
+                rs0 += p0;
+                rs1 += p1;
+                pb[rb][r >> 3][r & 7] = (__bf16)p0;
+                pb[rb][r >> 3][(r & 7) + 1] = (__bf16)p1;
+            }
+            l_run[rb] += rs0 + rs1;
         }
-        l_run += rs0 + rs1;
 #pragma unroll
         for (int st = 0; st < BC / 16; ++st) {
 #pragma unroll
-            for (int t = 0; t < D / 32; ++t) {
+            for (int t = 0; t < TB; ++t) {
                 const i16x4 lo = lds_read_tr16(Vs + L::v_read(st, t, 0, lane));
                 const i16x4 hi = lds_read_tr16(Vs + L::v_read(st, t, 1, lane));
                 const i16x4 w[2] = {lo, hi};
-                acc[t] = mfma32(__builtin_bit_cast(bf16x8, w), pb[st], acc[t]);
+                const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[rb][t] = mfma32(vop, pb[rb][st], acc[rb][t]);
             }
         }
     }
 
-    // Partials: acc[t] as 16 floats per lane, then m and l per lane, in this
-    // wave's own (now idle) slots.
+    // Partials: acc[rb][t] as 16 floats per lane in this wave's own (now idle)
+    // slots, (m, l) per row block in the table after the slots.
     float *const part = reinterpret_cast<float *>(Kw);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-        f32x4 *dst = reinterpret_cast<f32x4 *>(part + (t * 64 + lane) * 16);
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = f32x4{acc[t][4 * e], acc[t][4 * e + 1], acc[t][4 * e + 2], acc[t][4 * e + 3]};
+        for (int t = 0; t < TB; ++t) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(part + ((rb * TB + t) * 64 + lane) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[e] = f32x4{acc[rb][t][4 * e], acc[rb][t][4 * e + 1], acc[rb][t][4 * e + 2], acc[rb][t][4 * e + 3]};
+        }
+        // A wave that saw no allowed key of this row (all its tiles masked for
+        // it) holds a placeholder reference; -inf keeps it out of the combined
+        // maximum.  The test uses the row total so both lane halves agree.
+        ml[((wave * RB + rb) * 2) * 64 + lane] = pair_sum(l_run[rb]) > 0.f ? m_run[rb] : -INFINITY;
+        ml[((wave * RB + rb) * 2 + 1) * 64 + lane] = l_run[rb];
     }
-    // A wave that saw no allowed key of this row (all its tiles masked for it)
-    // holds a placeholder reference; -inf keeps it out of the combined maximum.
-    // The test uses the row total so both lane halves of a row agree.
-    part[32 * D + lane] = pair_sum(l_run) > 0.f ? m_run : -INFINITY;
-    part[32 * D + 64 + lane] = l_run;
     __syncthreads();
 
-    if (wave < D / 32) {
-        const int t = wave;
-        const float *pw[4];
+    if (wave < RB * TB) {
+        const int rb = wave / TB, t = wave - rb * TB;
+        const int qrow = r0 + 32 * rb + l32;
+        float mw[SW], m = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pw[w] = reinterpret_cast<const float *>(smem + w * WREG);
-        float mw[4], m = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            mw[w] = pw[w][32 * D + lane];
+        for (int w = 0; w < SW; ++w) {
+            mw[w] = ml[((w * RB + rb) * 2) * 64 + lane];
             m = fmaxf(m, mw[w]);
         }
         float l = 0.f;
         f32x16 o = f32x16{};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < SW; ++w) {
             const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - m);
-            l += f * pw[w][32 * D + 64 + lane];
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(pw[w] + (t * 64 + lane) * 16);
+            l += f * ml[((w * RB + rb) * 2 + 1) * 64 + lane];
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(smem + w * WREG) +
+                                                               ((rb * TB + t) * 64 + lane) * 16);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const f32x4 x = src[e];
@@ -565,8 +592,8 @@ __global__ __launch_bounds__(256) void split_kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_split(const FwdArgs &a, hipStream_t s) {
+template <int D, bool CAUSAL, int SW, int RB>
+hipError_t launch_split_shape(const FwdArgs &a, hipStream_t s) {
     Params p;
     p.q = static_cast<const uint16_t *>(a.q);
     p.k = static_cast<const uint16_t *>(a.k);
@@ -574,12 +601,26 @@ hipError_t launch_split(const FwdArgs &a, hipStream_t s) {
     p.o = static_cast<uint16_t *>(a.o);
     p.lse = a.lse;
     p.N = a.N;
-    p.nqb = (a.N + 31) / 32;
+    p.nqb = (a.N + 32 * RB - 1) / (32 * RB);
     p.scale_log2 = a.scale * kLog2e;
     p.paired = 0;
     const unsigned blocks = (unsigned)a.BH * (unsigned)p.nqb;
-    hipLaunchKernelGGL((split_kernel<D, CAUSAL>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((split_kernel<D, CAUSAL, SW, RB>), dim3(blocks), dim3(64 * SW), 0, s, p);
     return hipGetLastError();
+}
+
+// Non-causal d = 64: 8 waves x 64 rows when the 4-wave grid would exceed one
+// workgroup per CU, or when each of its waves would walk 16 or more tiles in
+// turn (measured: 1x12x1024 -9 %, 1x3x2048 -6 %, 1x1x4096 -14 %; grids of
+// up to one workgroup per CU with shorter walks were 15-68 % slower).
+template <int D, bool CAUSAL>
+hipError_t launch_split(const FwdArgs &a, hipStream_t s) {
+    if constexpr (D == 64 && !CAUSAL) {
+        const long long grid4 = (long long)a.BH * ((a.N + 31) / 32);
+        const int walk4 = ((a.N + 31) / 32 + 3) / 4;
+        if (grid4 > 256 || walk4 >= 16) return launch_split_shape<64, false, 8, 2>(a, s);
+    }
+    return launch_split_shape<D, CAUSAL, 4, 1>(a, s);
 }
 
 template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>

@@ -183,6 +183,21 @@ def test_causal_odd_block_count_eight_waves(ea, W, oracle_mod):
     assert torch.isfinite(o).all().item()
 
 
+@pytest.mark.parametrize("N", [4100, 2049])
+def test_wide_split_ragged(ea, W, oracle_mod, N):
+    # Non-causal d = 64 on a small grid with long key walks (one slice; 16 or
+    # more 32-key tiles per wave at four waves) runs the split-key kernel with
+    # 8 waves x 64 rows: every K and V operand feeds two 32-row blocks and
+    # eight partial states are merged.  Ragged N ends in a partial tile and a
+    # partial 64-row block.  Every row is checked.
+    B, H, d = 1, 1, 64
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=40 + N)
+    say(f"[parity] wide split-key B={B} H={H} N={N} d={d}")
+    ro, rl = oracle_mod.attention(q, k, v, 1 / math.sqrt(d), False)
+    o, lse = run(ea, q, k, v, False)
+    check_bf16(o, lse, ro, rl, "fused, 8-wave split-key")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_eight_wave_ragged(ea, W, oracle_mod, d, causal):
