@@ -201,13 +201,25 @@ def test_wide_split_ragged(ea, W, oracle_mod, N):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_eight_wave_ragged(ea, W, oracle_mod, d, causal):
-    # Grids of at least 1024 256-row blocks (and, causal, N > 4096) select the
+    # Grids of at least 192 256-row blocks (and, causal, N > 1024) select the
     # 8-wave K-ahead kernels; N = 1000 and 4100 end in a partial 64-key tile,
     # so the last steps take the checked path (masked tail keys, and for
     # causal the diagonal), after the unchecked main loop.  Rows come from
     # the first block, tile and block boundaries and the ragged end.
     N = 4100 if causal else 1000
     B, H = (1, 64) if causal else (4, 64)
+    _eight_wave_case(ea, W, oracle_mod, B, H, N, d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_eight_wave_causal_unpaired_mid_length(ea, W, oracle_mod, d):
+    # Causal N = 1500 on 64 slices: 6 blocks of 256 rows per slice, 384
+    # workgroups (at least 192 and N > 1024: the 8-wave kernel; fewer than two
+    # rounds: unpaired, longest block first), ragged last tile and block.
+    _eight_wave_case(ea, W, oracle_mod, 1, 64, 1500, d, True)
+
+
+def _eight_wave_case(ea, W, oracle_mod, B, H, N, d, causal):
     q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=900 + d + causal)
     rows = sorted({0, 1, 63, 64, 255, 256, N // 2, N - 66, N - 65, N - 64, N - 5, N - 1})
     slices = [0, 37, B * H - 1]
