@@ -138,6 +138,41 @@ def bench_fused_graph(ea, w, calls=20, replays=5):
     return ms
 
 
+def bench_fused_cold(ea, w, calls=10, flush_bytes=512 << 20):
+    """Per-call time with a 512 MiB buffer written between calls, so the
+    inputs are not served from L2 or the MALL; the event pair brackets only
+    the attention call."""
+    import torch
+    from exact_attention_124_amd.workloads import workload_inputs
+    q, k, v = workload_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=q.device)
+    fn = getattr(ea, "attn_fwd" if w.dtype == torch.bfloat16 else "attn_fwd_f32")
+    stream = torch.cuda.current_stream()
+    fn(q, k, v, o, lse, causal=w.causal, stream=stream)
+    per = []
+    for _ in range(calls):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(q, k, v, o, lse, causal=w.causal, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    del q, k, v, o, lse, flush
+    torch.cuda.empty_cache()
+    return sorted(per)[len(per) // 2]
+
+
+def device_info():
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip,
+            "memory_GiB": round(props.total_memory / (1 << 30), 1)}
+
+
 def bench_fused(ea, w, steps, warmup):
     import torch
     from exact_attention_124_amd.workloads import workload_inputs
@@ -420,6 +455,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded iid N(0,1) Q, K, V, rounded to bf16)",
+        "device": device_info(),
         "config": {"workload": f"{w.name}: {w.describe()}", "B": w.B, "H": w.H, "N": w.N,
                    "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -449,6 +485,10 @@ def main():
             if gm is not None:
                 sweep[-1].update({"graph_ms_per_call": round(gm, 4),
                                   "graph_TFLOP/s": round(ww.flops / (gm * 1e-3) / 1e12, 2)})
+            if name in ("gpt2_heads_bf16", "causal_2k_bf16"):
+                cm = bench_fused_cold(ea, ww)
+                sweep[-1].update({"cold_launch_ms": round(cm, 4),
+                                  "cold_note": "median of 10 calls, each after a 512 MiB buffer write"})
             log(f"[bench] sweep {name}: {lm:.4f} ms per launch"
                 + (f", {gm:.4f} ms per call in a graph" if gm is not None else "")
                 + f", {sweep[-1]['TFLOP/s']} TFLOP/s")
