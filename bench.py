@@ -363,10 +363,21 @@ def cpu_baseline(w, target_s=15.0):
     secs = time.perf_counter() - t0
     keys = (w.N * (w.N + 1) // 2) if w.causal else w.N * w.N
     flops = 4.0 * w.d * keys * n_sl
+    # The fp32 1x1x128x64 workload whole, on one thread (median of 5 runs).
+    from exact_attention_124_amd.workloads import WORKLOADS
+    ws = WORKLOADS["small_fp32"]
+    qs, ks, vs = make_qkv(ws.B, ws.H, ws.N, ws.d, ws.dtype, ws.seed, ws.q_mult)
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.attention(qs, ks, vs, ws.scale, ws.causal, threads=1)
+        ts.append(time.perf_counter() - t0)
+    small_ms = sorted(ts)[2] * 1e3
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"{w.name}: all {w.N} query rows of {n_sl} seeded (b,h) slices of {w.B * w.H}, "
                        f"fp64, {secs:.1f} s"),
-            "seconds": round(secs, 3), "flop": flops}
+            "seconds": round(secs, 3), "flop": flops,
+            "small_fp32_one_thread_ms": round(small_ms, 3)}
 
 
 def n_sweep(ea):
