@@ -411,6 +411,8 @@ def main():
                     help="only the masked / biased forward legs")
     ap.add_argument("--fp8-only", action="store_true",
                     help="only the fp8 forward legs (for kernel traces of that kernel)")
+    ap.add_argument("--fused-only", metavar="WORKLOAD", default=None,
+                    help="only time the fused forward on the named workload (for counter runs on it)")
     ap.add_argument("--n-sweep", action="store_true",
                     help="only run fused and unfused once each at B=1 H=32 d=128 for N = 1k..16k "
                          "(for HBM byte counters), plus the copy calibration")
@@ -438,6 +440,13 @@ def main():
         return
     if args.masked_only:
         print(json.dumps({"masked": masked_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
+        return
+    if args.fused_only:
+        ww = WORKLOADS[args.fused_only]
+        tot, pl = bench_fused(ea, ww, args.steps, args.warmup)
+        lm = sum(pl) / len(pl)
+        print(json.dumps({"fused": {"workload": ww.name, "desc": ww.describe(), "launch_ms": round(lm, 4),
+                                    "TFLOP/s": round(ww.flops / (lm * 1e-3) / 1e12, 2)}}), flush=True)
         return
     if args.fp8_only:
         print(json.dumps({"fp8": fp8_legs(ea, WORKLOADS, args.steps, args.warmup)}), flush=True)
