@@ -113,35 +113,46 @@ def _torch():
 
 def _check_qkv(q, k, v, dtype):
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v)):
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    shape = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must live on a GPU")
+    if q.dtype != dtype:
+        raise TypeError(f"q must be {dtype}, got {q.dtype}")
+    if len(shape) != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, N, d] tensor")
+    for name, t in (("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must live on a GPU")
         if t.dtype != dtype:
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if t.dim() != 4 or not t.is_contiguous():
+        if t.shape != shape:
+            raise ValueError("q, k and v must have the same shape")
+        if t.device != dev:
+            raise ValueError("q, k and v must be on the same device")
+        if not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k and v must have the same shape")
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k and v must be on the same device")
-    return tuple(q.shape)
+    return tuple(shape)
 
 
 def _check_out(o, lse, shape, dtype, device):
     torch = _torch()
-    if o.dtype != dtype or tuple(o.shape) != shape or not o.is_contiguous() or o.device != device:
+    if o.dtype != dtype or o.shape != shape or o.device != device or not o.is_contiguous():
         raise ValueError("o must be a contiguous tensor like q")
     if lse is not None:
-        if lse.dtype != torch.float32 or tuple(lse.shape) != shape[:3] or not lse.is_contiguous() \
-                or lse.device != device:
+        if lse.dtype != torch.float32 or lse.shape != shape[:3] or lse.device != device \
+                or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
 
 
 def _stream(stream, device):
-    torch = _torch()
     if stream is None:
+        torch = _torch()
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:  # the current stream's handle, without building a Stream object
+            return raw(device.index if device.index is not None else torch.cuda.current_device())
         return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
@@ -158,8 +169,12 @@ def _ptr(t):
 
 def _launch(device, fn, *args):
     """Call a C entry point with ``device`` current: its kernels are launched
-    on the current device, which must own the tensors and the stream."""
-    with _torch().cuda.device(device):
+    on the current device, which must own the tensors and the stream.  The
+    device is switched (and restored) only when another one is current."""
+    torch = _torch()
+    if device.index is None or device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
         return fn(*args)
 
 

@@ -252,18 +252,19 @@ void kernel(Params p) {
 #pragma unroll
                 for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
             }
+            // The row sum adds the probabilities as rounded for P*V.
             float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
+                u32x4 w[2];
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
                     const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
-                    rs0 += p0;
-                    rs1 += p1;
-                    pb[2 * b + (r >> 3)][r & 7] = (__bf16)p0;
-                    pb[2 * b + (r >> 3)][(r & 7) + 1] = (__bf16)p1;
+                    w[r >> 3][(r & 7) >> 1] = pack_sum_bf16x2(p0, p1, (r & 2) ? rs1 : rs0);
                 }
+                pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
+                pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
             }
             l_run += rs0 + rs1;
         };
@@ -506,15 +507,15 @@ __global__ __launch_bounds__(64 * SW) void split_kernel(Params p) {
                 for (int t = 0; t < TB; ++t) acc[rb][t] *= alpha;
             }
             float rs0 = 0.f, rs1 = 0.f;
+            u32x4 w[2];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = fast_exp2(fmaf(sc[rb][r], c, -m_run[rb]));
                 const float p1 = fast_exp2(fmaf(sc[rb][r + 1], c, -m_run[rb]));
-                rs0 += p0;
-                rs1 += p1;
-                pb[rb][r >> 3][r & 7] = (__bf16)p0;
-                pb[rb][r >> 3][(r & 7) + 1] = (__bf16)p1;
+                w[r >> 3][(r & 7) >> 1] = pack_sum_bf16x2(p0, p1, (r & 2) ? rs1 : rs0);
             }
+            pb[rb][0] = __builtin_bit_cast(bf16x8, w[0]);
+            pb[rb][1] = __builtin_bit_cast(bf16x8, w[1]);
             l_run[rb] += rs0 + rs1;
         }
 #pragma unroll

@@ -128,13 +128,18 @@ void kernel(Params p) {
         qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
 
     // Bias rows of this wave: a resource over rows q0 .. min(q0 + 31, N - 1).
+    // A wave of the last block may start at or past row N (it holds padding
+    // rows only); its resource is empty, so every bias load returns zero and
+    // none of them touches memory beyond the bias tensor.
     const float *bbase = p.bias;
     uint32_t bbytes = 0;
     if constexpr (BIAS) {
-        const int b_idx = bh / p.H, h_idx = bh - b_idx * p.H;
-        bbase = p.bias + (long long)b_idx * p.sb + (long long)h_idx * p.sh + (long long)q0 * p.si;
-        const int rows = max(0, min(31, N - 1 - q0));
-        bbytes = (uint32_t)(((long long)rows * p.si + N) * 4);
+        if (q0 < N) {
+            const int b_idx = bh / p.H, h_idx = bh - b_idx * p.H;
+            bbase = p.bias + (long long)b_idx * p.sb + (long long)h_idx * p.sh + (long long)q0 * p.si;
+            const int rows = min(31, N - 1 - q0);
+            bbytes = (uint32_t)(((long long)rows * p.si + N) * 4);
+        }
     }
     const auto rb = make_rsrc(bbase, bbytes);
 
@@ -236,18 +241,20 @@ void kernel(Params p) {
         }
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;  // no finite score yet: every p is 0
         bf16x8 pb[2 * NB];
+        // The row sum adds the probabilities as rounded for P*V.
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+            u32x4 w[2];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = fast_exp2(fmaf(s[b][r], cu, -m_sub));
                 const float p1 = fast_exp2(fmaf(s[b][r + 1], cu, -m_sub));
-                rs0 += p0;
-                rs1 += p1;
-                pb[2 * b + (r >> 3)][r & 7] = (__bf16)p0;
-                pb[2 * b + (r >> 3)][(r & 7) + 1] = (__bf16)p1;
+                w[r >> 3][(r & 7) >> 1] = pack_sum_bf16x2(p0, p1, (r & 2) ? rs1 : rs0);
             }
+            pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
+            pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
+        }
         l_run += rs0 + rs1;
         // O^T += V_tile^T P^T.
         const uint16_t *Vs = Vbuf + buf * T::TILE;

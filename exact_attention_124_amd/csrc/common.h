@@ -117,6 +117,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two probabilities rounded to bf16 (nearest even) and packed low/high, the
+// word the P*V product consumes; their sum as rounded is added to `acc` with
+// one v_dot2c_f32_bf16 against (1, 1).  Normalising O by the sum of the
+// rounded probabilities makes it a weighted mean of V rows whose weights add
+// up to one: the rounding of a dominant probability then cancels between the
+// numerator and the denominator instead of moving O by up to 2^-8 |v|.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_sum_bf16x2(float lo, float hi, float &acc) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -2,8 +2,9 @@
 the fp64 oracle (oracle.attention_masked) on the same seeded inputs.
 
 Tolerances are those of the bf16 fused kernel: over every checked element
-max|dO| <= 2e-2 and mean|dO| <= 2e-3, |dlse| <= 1e-3; the bias is added in
-fp32, so it adds no bf16 rounding.  Rows with no allowed finite score must
+max|dO| <= 2e-2 and mean|dO| <= 2e-3, |dlse| <= 4e-3 (the row sum adds the
+bf16-rounded probabilities, each within 2^-8 of its fp32 value); the bias is
+added in fp32, so it adds no bf16 rounding.  Rows with no allowed finite score must
 come out as exactly 0 with lse = -inf.
 """
 import math
@@ -15,7 +16,7 @@ import torch
 
 pytestmark = pytest.mark.gpu
 
-MAX_ERR, MEAN_ERR, LSE_ERR = 2e-2, 2e-3, 1e-3
+MAX_ERR, MEAN_ERR, LSE_ERR = 2e-2, 2e-3, 4e-3
 
 
 def say(msg):
@@ -149,3 +150,19 @@ def test_per_head_bias_large_grid(ea, W, oracle_mod):
         ro, rl = oracle_mod.attention_masked(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
                                              1 / math.sqrt(d), False, -1, -1, bias[:, h:h + 1], rows=rows)
         check(o[b:b + 1, h:h + 1, r].cpu(), lse[b:b + 1, h:h + 1, r].cpu(), ro, rl, f"per-head bias b={b} h={h}")
+
+
+def test_ragged_bias_tail_waves(ea, W, oracle_mod):
+    # N = 8200 = 64 * 128 + 8: the last 128-row block holds 8 real rows, so
+    # three of its four waves start at or past row N and must read no bias at
+    # all.  A contiguous [N, N] bias with no window and no causal mask keeps
+    # every tile active for those waves.  Every row of both slices is checked.
+    B, H, N, d = 1, 2, 8200, 128
+    say(f"[masked] ragged tail waves, [N, N] bias, B={B} H={H} N={N}")
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=12)
+    bias = W.make_bias(1, 1, N, seed=13, scale=1.0, drop=0.05)
+    bd = bias[0, 0].contiguous().cuda()
+    o, lse = ea.attention_masked(q.cuda(), k.cuda(), v.cuda(), causal=False, bias=bd)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.attention_masked(q, k, v, 1 / math.sqrt(d), False, -1, -1, bias)
+    check(o, lse, ro, rl, "N=8200 [N,N] bias")

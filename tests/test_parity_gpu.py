@@ -4,10 +4,13 @@ same seeded inputs.
 Tolerances (bf16 inputs, unit-variance data): over every checked element,
 max|dO| <= 2e-2 and mean|dO| <= 2e-3.  fp32 path: max|dO| <= 1e-5 * max|O_ref|
 (normwise; an element-wise relative bound is ill-posed where O ~ 0).  lse:
-fused bf16 |dlse| <= 1e-3 (it is computed from fp32 scores); fp32
-|dlse| <= 1e-5 * max(1, |lse|); unfused bf16 scores are rounded to bf16 before
-the softmax, so its lse may move by up to 2^-8 of the largest |scaled score|
-(bounded by scale * max|q| * max|k|).
+the fused bf16 kernel's row sum adds the probabilities as rounded to bf16 for
+P*V, each within 2^-8 of its fp32 value, so ln(sum) moves by at most
+ln(1 + 2^-8) = 3.9e-3 (scores and sums are fp32, adding well under 1e-4):
+|dlse| <= 4e-3; fp32 |dlse| <= 1e-5 * max(1, |lse|); unfused bf16 scores are
+rounded to bf16 before the softmax (whose sum is fp32), so its lse may move by
+up to 2^-8 of the largest |scaled score| (bounded by scale * max|q| * max|k|)
+plus 1e-3.
 """
 import math
 import sys
@@ -18,7 +21,8 @@ import torch
 
 pytestmark = pytest.mark.gpu
 
-BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 1e-3
+BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 4e-3
+UNFUSED_LSE_BASE = 1e-3
 F32_REL = 1e-5
 
 
@@ -70,7 +74,7 @@ def check_f32(o, lse, ro, rl, what):
 def unfused_lse_tol(q, k, scale):
     qn = q.float().norm(dim=-1).max().item()
     kn = k.float().norm(dim=-1).max().item()
-    return 2.0 ** -8 * scale * qn * kn + BF16_LSE
+    return 2.0 ** -8 * scale * qn * kn + UNFUSED_LSE_BASE
 
 
 def run(ea, q, k, v, causal, scale=None, variant="fused"):
@@ -109,22 +113,24 @@ def test_gpt2_heads_bf16_full(ea, W, oracle_mod):
     check_bf16(o, lse, ro, rl, "unfused bf16", unfused_lse_tol(q, k, w.scale))
 
 
-def _sampled(ea, W, oracle_mod, name, rows_per_slice, extra_rows, variants=("fused",)):
+def _named_slices(ea, W, oracle_mod, name, extra_rows, variants=("fused",)):
+    # Every row of the slices the workload names for the oracle (all slices
+    # when it names none) is compared element by element; a few seeded rows
+    # of every other slice are checked as well.
     w = W.WORKLOADS[name]
-    say(f"[parity] {w.describe()} (sampled rows)")
+    slices = W.check_slices(w)
+    say(f"[parity] {w.describe()}: every row of {len(slices)} slices")
     q, k, v = W.workload_inputs(w)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    slices = W.check_slices(w)
-    rows = W.sample_rows(w.N, rows_per_slice, seed=2)
-    H = w.H
     qs = q.reshape(-1, w.N, w.d)[slices]
     ks = k.reshape(-1, w.N, w.d)[slices]
     vs = v.reshape(-1, w.N, w.d)[slices]
-    ro, rl = oracle_mod.attention(qs, ks, vs, w.scale, w.causal, rows=rows)
-    # a few rows of every slice, too
+    ro, rl = oracle_mod.attention(qs, ks, vs, w.scale, w.causal)
+    say(f"  oracle done on {len(slices)} full slices")
     all_rows = W.sample_rows(w.N, extra_rows, seed=3)
     ro2, rl2 = oracle_mod.attention(q.reshape(-1, w.N, w.d), k.reshape(-1, w.N, w.d),
                                     v.reshape(-1, w.N, w.d), w.scale, w.causal, rows=all_rows)
+    del qs, ks, vs
     for variant in variants:
         if variant == "fused":
             o, lse = ea.attention(qd, kd, vd, causal=w.causal)
@@ -137,9 +143,7 @@ def _sampled(ea, W, oracle_mod, name, rows_per_slice, extra_rows, variants=("fus
         of = o.reshape(-1, w.N, w.d)
         lf = lse.reshape(-1, w.N)
         sl = torch.tensor(slices, device=o.device)
-        rw = torch.tensor(rows, device=o.device)
-        check_bf16(of[sl][:, rw], lf[sl][:, rw], ro, rl,
-                   f"{variant} {len(slices)} slices x {len(rows)} rows", tol)
+        check_bf16(of[sl], lf[sl], ro, rl, f"{variant} {len(slices)} slices x all {w.N} rows", tol)
         arw = torch.tensor(all_rows, device=o.device)
         check_bf16(of[:, arw], lf[:, arw], ro2, rl2,
                    f"{variant} all {of.shape[0]} slices x {len(all_rows)} rows", tol)
@@ -150,18 +154,18 @@ def _sampled(ea, W, oracle_mod, name, rows_per_slice, extra_rows, variants=("fus
     torch.cuda.empty_cache()
 
 
-def test_causal_2k_bf16_sampled(ea, W, oracle_mod):
-    _sampled(ea, W, oracle_mod, "causal_2k_bf16", 96, 8, variants=("fused", "unfused"))
+def test_causal_2k_bf16_every_slice(ea, W, oracle_mod):
+    _named_slices(ea, W, oracle_mod, "causal_2k_bf16", 8, variants=("fused", "unfused"))
 
 
-def test_dense_8k_bf16_sampled(ea, W, oracle_mod):
-    _sampled(ea, W, oracle_mod, "dense_8k_bf16", 256, 6, variants=("fused", "unfused"))
+def test_dense_8k_bf16_named_slices(ea, W, oracle_mod):
+    _named_slices(ea, W, oracle_mod, "dense_8k_bf16", 6, variants=("fused", "unfused"))
 
 
-def test_causal_32k_qx8_bf16_sampled(ea, W, oracle_mod):
+def test_causal_32k_qx8_bf16_named_heads(ea, W, oracle_mod):
     # The unfused path is not parity-gated here: its bf16 scores carry absolute
     # errors of ~0.25 at logits near 32, beyond the 2e-2 output bound.
-    _sampled(ea, W, oracle_mod, "causal_32k_qx8_bf16", 256, 4)
+    _named_slices(ea, W, oracle_mod, "causal_32k_qx8_bf16", 4)
 
 
 def test_causal_odd_block_count_eight_waves(ea, W, oracle_mod):
@@ -375,7 +379,7 @@ def test_key_permutation_invariance(ea, W):
     o1, l1 = run(ea, q, k, v, False)
     o2, l2 = run(ea, q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False)
     assert (o1.float() - o2.float()).abs().max().item() <= BF16_MAX
-    assert (l1 - l2).abs().max().item() <= BF16_LSE
+    assert (l1 - l2).abs().max().item() <= 2 * BF16_LSE  # two results, each within BF16_LSE
 
 
 def test_deterministic(ea, W):
@@ -440,6 +444,6 @@ def test_schedule_independence(ea, W):
             d_l = (l1[0, 0] - l_all[b, h]).abs().max().item()
             say(f"  split-key vs regular: max|dO|={d_o.max().item():.3e} mean={d_o.mean().item():.3e} "
                 f"max|dlse|={d_l:.3e}")
-            assert d_o.max().item() <= BF16_MAX and d_o.mean().item() <= BF16_MEAN and d_l <= BF16_LSE
+            assert d_o.max().item() <= BF16_MAX and d_o.mean().item() <= BF16_MEAN and d_l <= 2 * BF16_LSE
         del q, k, v, o_all, l_all
         torch.cuda.empty_cache()
