@@ -20,6 +20,7 @@ __all__ = [
     "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
     "attn_bwd_workspace_bytes", "attention_backward", "attn_fwd_fp8", "attention_fp8",
     "attn_fwd_masked", "attention_masked", "ew_chain_fused", "ew_chain_unfused", "elementwise_chain",
+    "attn_bwd_noalloc", "BWD_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,8 +31,10 @@ _lib = None
 STATUS = {
     "ATTN_OK": 0, "ATTN_ERR_NULL": 1, "ATTN_ERR_SHAPE": 2, "ATTN_ERR_HEAD_DIM": 3,
     "ATTN_ERR_ALIGN": 4, "ATTN_ERR_ALIAS": 5, "ATTN_ERR_WORKSPACE": 6, "ATTN_ERR_HIP": 7,
-    "ATTN_ERR_ARG": 8,
+    "ATTN_ERR_ARG": 8, "ATTN_ERR_SCRATCH": 9,
 }
+# ATTN_BWD_SCRATCH_BYTES (include/attn.h): attn_bwd_noalloc's static statistics buffer per GPU
+BWD_SCRATCH_BYTES = 16 << 20
 
 
 class AttnError(RuntimeError):
@@ -75,6 +78,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_fp8.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
     lib.attn_bwd.restype = I
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.attn_bwd_noalloc.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = SZ
     lib.attn_unfused_workspace_bytes.argtypes = [I, I, I, I]
@@ -331,6 +336,28 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=N
                  B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None, stream=None):
+    """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv`` with the
+    statistics in the library's static per-GPU scratch (no workspace, no
+    allocation).  Calls that overlap on one GPU race on that scratch."""
+    torch = _torch()
+    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
+    _check_qkv(o, dout, dout, torch.bfloat16)
+    if tuple(o.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d):
+        raise ValueError("o and dout must have q's shape")
+    for t in (dq, dk, dv):
+        _check_out(t, None, (B, H, N, d), torch.bfloat16, q.device)
+    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
+    if lse is None:
+        raise ValueError("lse (the forward's log-sum-exp) is required")
+    st = _launch(q.device, load_library().attn_bwd_noalloc,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
 
 
 # ---------------------------------------------------------------------------

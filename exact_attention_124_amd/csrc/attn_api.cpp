@@ -141,29 +141,57 @@ int validate_ew(const void *x, const void *y, const float *bias, long long rows,
     return ATTN_OK;
 }
 
+// Backward checks.  ws == nullptr with ws_bytes == 0 means "no caller
+// workspace" (attn_bwd_noalloc): the workspace null, size, alignment and
+// overlap checks are skipped.
 int validate_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                  const void *dq, const void *dk, const void *dv, const void *ws, size_t ws_bytes, int B, int H,
-                 int N, int d, float scale, int causal) {
+                 int N, int d, float scale, int causal, bool caller_workspace) {
     const int st = validate_common(q, k, v, o, lse, B, H, N, d, scale, causal, 2, 2);
     if (st != ATTN_OK) return st;
-    if (!lse || !dout || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
-    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(ws, 16))
+    if (!lse || !dout || !dq || !dk || !dv || (caller_workspace && !ws)) return ATTN_ERR_NULL;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        (caller_workspace && !aligned(ws, 16)))
         return ATTN_ERR_ALIGN;
     const size_t need = attn_bwd_workspace_bytes(B, H, N);
-    if (need == 0 || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (need == 0 || (caller_workspace && ws_bytes < need)) return ATTN_ERR_WORKSPACE;
     // Grid of the statistics launch: 16 padded rows per workgroup.
     if ((uint64_t)B * H * ((uint64_t)(N + 31) / 32 * 32) / 16 >= (1ull << 31)) return ATTN_ERR_SHAPE;
     const size_t tensor = (size_t)B * H * (size_t)N * d * 2;
     const Range in[6] = {range_of(q, tensor), range_of(k, tensor), range_of(v, tensor), range_of(o, tensor),
                          range_of(dout, tensor), range_of(lse, (size_t)B * H * (size_t)N * sizeof(float))};
-    const Range out[4] = {range_of(dq, tensor), range_of(dk, tensor), range_of(dv, tensor), range_of(ws, need)};
-    for (int i = 0; i < 4; ++i) {
+    const int nout = caller_workspace ? 4 : 3;
+    const Range out[4] = {range_of(dq, tensor), range_of(dk, tensor), range_of(dv, tensor),
+                          caller_workspace ? range_of(ws, need) : Range{0, 0}};
+    for (int i = 0; i < nout; ++i) {
         for (int j = 0; j < 6; ++j)
             if (overlaps(out[i], in[j])) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < nout; ++j)
             if (overlaps(out[i], out[j])) return ATTN_ERR_ALIAS;
     }
     return ATTN_OK;
+}
+
+attn::BwdArgs make_bwd_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv, void *workspace, int B, int H, int N,
+                            int d, float scale, int causal) {
+    attn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.stats = static_cast<float *>(workspace);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.BH = B * H;
+    a.N = N;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    return a;
 }
 
 }  // namespace
@@ -270,25 +298,23 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
     if (B == 0 || H == 0 || N == 0) return ATTN_OK;
     const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale,
-                                causal);
+                                causal, true);
     if (st != ATTN_OK) return st;
-    attn::BwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.dout = dout;
-    a.lse = lse;
-    a.stats = static_cast<float *>(workspace);
-    a.dq = dq;
-    a.dk = dk;
-    a.dv = dv;
-    a.BH = B * H;
-    a.N = N;
-    a.d = d;
-    a.scale = scale;
-    a.causal = causal;
-    return finish(attn::launch_bwd_bf16(a, stream));
+    return finish(attn::launch_bwd_bf16(
+        make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal), stream));
+}
+
+int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d, float scale,
+                     int causal, hipStream_t stream) {
+    static_assert(ATTN_BWD_SCRATCH_BYTES == ((size_t)16 << 20), "header and library must agree");
+    if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || H == 0 || N == 0) return ATTN_OK;
+    const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, 0, B, H, N, d, scale, causal, false);
+    if (st != ATTN_OK) return st;
+    if (attn_bwd_workspace_bytes(B, H, N) > attn::bwd_scratch_bytes()) return ATTN_ERR_SCRATCH;
+    return finish(attn::launch_bwd_bf16_noalloc(
+        make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, H, N, d, scale, causal), stream));
 }
 
 int ew_chain_fused(const void *x, void *y, const float *bias, long long rows, int cols, float scale,
@@ -318,6 +344,9 @@ const char *attn_status_string(int status) {
         case ATTN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() reports";
         case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
         case ATTN_ERR_ARG: return "scale and fp8 descale factors must be finite and > 0, causal must be 0 or 1";
+        case ATTN_ERR_SCRATCH:
+            return "attn_bwd_noalloc: B*H*round_up(N,32) rows of statistics exceed its static scratch "
+                   "(ATTN_BWD_SCRATCH_BYTES); use attn_bwd with a workspace";
         default: return "unknown status";
     }
 }

@@ -33,6 +33,9 @@
 #include "common.h"
 #include "launch.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace attn {
 namespace bwd_bf16 {
 
@@ -521,6 +524,56 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s) {
     using namespace bwd_bf16;
     if (a.d == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
     return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Statistics without a workspace argument: a static device array, one copy per
+// GPU, that every attn_bwd_noalloc call on that GPU reuses.  In host code the
+// name `scratch` is only a stand-in for the symbol; the device address of the
+// current GPU's copy comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and only that address is handed to kernels.  The
+// statistics kernel writes every entry the other two kernels read (zeros for
+// padding rows), so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_for_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_bwd_bf16_noalloc(BwdArgs a, hipStream_t s) {
+    void *p = nullptr;
+    const hipError_t e = scratch_for_current_device(&p);
+    if (e != hipSuccess) return e;
+    a.stats = static_cast<float *>(p);
+    return launch_bwd_bf16(a, s);
 }
 
 }  // namespace attn

@@ -77,6 +77,11 @@ struct BwdArgs {
 
 // Backward: row statistics, then dK/dV, then dQ (three launches).
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t s);
+// The same launches with the statistics in the library's static per-device
+// scratch array (a.stats is ignored); the caller has checked that
+// attn_bwd_workspace_bytes() fits bwd_scratch_bytes().
+hipError_t launch_bwd_bf16_noalloc(BwdArgs a, hipStream_t s);
+size_t bwd_scratch_bytes();
 
 // Elementwise chain y = relu(scale * x + bias) over a [rows, cols] bf16
 // tensor (cols a multiple of 8), fused (one launch) or as three launches.

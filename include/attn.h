@@ -55,7 +55,8 @@ typedef enum {
     ATTN_ERR_ALIAS = 5,     /* an output range overlaps an input or another output range   */
     ATTN_ERR_WORKSPACE = 6, /* workspace smaller than attn_unfused_workspace_bytes / attn_bwd_workspace_bytes */
     ATTN_ERR_HIP = 7,       /* a HIP runtime call failed (see attn_last_hip_error)        */
-    ATTN_ERR_ARG = 8        /* scale (or an fp8 descale) not finite and > 0, or causal not 0/1 */
+    ATTN_ERR_ARG = 8,       /* scale (or an fp8 descale) not finite and > 0, or causal not 0/1 */
+    ATTN_ERR_SCRATCH = 9    /* attn_bwd_noalloc: the statistics exceed the library's static scratch */
 } attn_status;
 
 /*
@@ -195,6 +196,30 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
 /* Workspace bytes attn_bwd needs: B*H*2*round_up(N, 32)*4.  Returns 0 for
  * non-positive arguments or on size_t overflow.  Pure host function. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The per-row statistics go to a static device array
+ * inside the library (ATTN_BWD_SCRATCH_BYTES per GPU, held until the process
+ * ends); nothing is allocated or freed by the call.
+ *   Arguments, layouts, results and the other checks are those of attn_bwd.
+ *   The statistics need attn_bwd_workspace_bytes(B, H, N) bytes; a problem
+ *   needing more than ATTN_BWD_SCRATCH_BYTES returns ATTN_ERR_SCRATCH and
+ *   enqueues nothing (B*H*round_up(N, 32) <= 2^21 rows fits, e.g.
+ *   8 x 32 x 8192).
+ *   On its first call on a device the library looks up that device's copy of
+ *   the array (hipGetSymbolAddress, with the device current); a failure there
+ *   returns ATTN_ERR_HIP.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (on different streams, or
+ *   from several threads without ordering) race on it and their results are
+ *   undefined.  Calls ordered on one stream are safe.
+ */
+#define ATTN_BWD_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv,
+                     int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char *attn_status_string(int status);

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_unfused", "attn_fwd_unfused_f32",
                             "attn_unfused_workspace_bytes", "attn_status_string",
-                            "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_fwd_masked"])
+                            "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_fwd_masked",
+                            "attn_bwd_noalloc"])
 
 
 def test_ew_header_declares_the_chain():
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import exact_attention_124_amd as ea
-    for code in range(9):
+    for code in range(10):
         s = ea.attn_status_string(code)
         assert s and s != "unknown status"
     assert ea.attn_status_string(99) == "unknown status"
@@ -257,6 +258,36 @@ def test_bwd_validation_codes(lib):
     assert bwd(lib, ws=L) == S["ATTN_ERR_ALIAS"]        # workspace over lse
     assert bwd(lib, ws=DK + 32) == S["ATTN_ERR_ALIAS"]  # workspace over an output
     assert bwd(lib, N=1 << 26, d=128) == S["ATTN_ERR_SHAPE"]
+
+
+def bwd_noalloc(lib, B=1, H=2, N=256, d=64, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, scale=0.125, causal=0)
+    args.update(kw)
+    return lib.attn_bwd_noalloc(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dout"],
+                                args["dq"], args["dk"], args["dv"], B, H, N, d, args["scale"], args["causal"],
+                                None)
+
+
+def test_bwd_noalloc_validation_codes(lib):
+    # The checks of attn_bwd without the workspace ones, then the static
+    # scratch limit (16 MiB of statistics: B*H*round_up(N, 32) <= 2^21 rows).
+    # Every call below fails validation or is empty: nothing is launched.
+    import exact_attention_124_amd as ea
+    S = ea.STATUS
+    for name in ("q", "o", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd_noalloc(lib, **{name: None}) == S["ATTN_ERR_NULL"], name
+    assert bwd_noalloc(lib, N=0) == S["ATTN_OK"]
+    assert bwd_noalloc(lib, N=-1) == S["ATTN_ERR_SHAPE"]
+    assert bwd_noalloc(lib, d=96) == S["ATTN_ERR_HEAD_DIM"]
+    assert bwd_noalloc(lib, scale=0.0) == S["ATTN_ERR_ARG"]
+    assert bwd_noalloc(lib, dq=DQ + 8) == S["ATTN_ERR_ALIGN"]
+    assert bwd_noalloc(lib, dq=Q) == S["ATTN_ERR_ALIAS"]
+    assert bwd_noalloc(lib, dv=DQ) == S["ATTN_ERR_ALIAS"]
+    # one padded row past the limit: 2^21 + 32 rows of statistics
+    assert ea.attn_bwd_workspace_bytes(1, 64, 32768) == ea.BWD_SCRATCH_BYTES
+    assert bwd_noalloc(lib, B=1, H=64, N=32768 + 1) == S["ATTN_ERR_SCRATCH"]
+    assert bwd_noalloc(lib, B=8, H=32, N=16384, d=128) == S["ATTN_ERR_SCRATCH"]
+    assert "scratch" in ea.attn_status_string(S["ATTN_ERR_SCRATCH"])
 
 
 def test_python_binding_rejects_cpu_tensors(lib):
