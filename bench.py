@@ -396,6 +396,69 @@ def n_sweep(ea):
     copy_calibration(reps=2)
 
 
+HEADLINE_KERNEL = "attn::fwd_bf16::persistent_kernel<128, false>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def write_traffic_record(fetch_csv: str, write_csv: str) -> dict:
+    """Turn two rocprofv3 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` counter
+    CSVs of ``bench.py --quick --calibrate-copy`` into the traffic record read
+    by the roofline entry: per-dispatch KiB of the headline kernel, each scaled
+    by what the same counter reads for the 1 GiB device copy (2**30 bytes read
+    and written).  Host-only; writes profiles/attn_fwd_bf16_dense_8k_traffic.json."""
+    import collections
+    import csv
+
+    def per_dispatch(path):
+        kern = collections.defaultdict(float)
+        copies = []
+        names = {}
+        copy_acc = collections.defaultdict(float)
+        for r in csv.DictReader(open(path)):
+            d = int(r["Dispatch_Id"])
+            if HEADLINE_KERNEL in r["Kernel_Name"]:
+                kern[d] += float(r["Counter_Value"])
+                names[d] = r["Kernel_Name"]
+            elif COPY_KERNEL in r["Kernel_Name"]:
+                copy_acc[d] += float(r["Counter_Value"])
+        copies = [copy_acc[d] for d in sorted(copy_acc)]
+        return [kern[d] for d in sorted(kern)], copies, next(iter(names.values()), None)
+
+    fetch, fcopy, kname = per_dispatch(fetch_csv)
+    write, wcopy, _ = per_dispatch(write_csv)
+    if not fetch or not write or not fcopy or not wcopy:
+        raise SystemExit("no headline-kernel or copy dispatches in the counter files")
+    # the 1 GiB copy dominates: take the largest copy dispatch of each run
+    fscale = (1 << 30) / 1024 / max(fcopy)
+    wscale = (1 << 30) / 1024 / max(wcopy)
+    fk = sum(fetch) / len(fetch)
+    wk = sum(write) / len(write)
+    w = __import__("exact_attention_124_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[HEADLINE]
+    rec = {
+        "kernel": kname,
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+        "fetch_kib_per_dispatch_each": fetch, "write_kib_per_dispatch_each": write,
+        "copy_fetch_kib_per_GiB": max(fcopy), "copy_write_kib_per_GiB": max(wcopy),
+        "fetch_scale": fscale, "write_scale": wscale,
+        "read_bytes_per_launch": fk * 1024 * fscale, "write_bytes_per_launch": wk * 1024 * wscale,
+        "bytes_per_launch": fk * 1024 * fscale + wk * 1024 * wscale,
+        "algorithmic_read_bytes": 3 * w.B * w.H * w.N * w.d * 2,
+        "algorithmic_write_bytes": w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- "
+            "python3 bench.py --quick --steps 3 --warmup 1 --calibrate-copy",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- "
+            "python3 bench.py --quick --steps 3 --warmup 1 --calibrate-copy",
+            f"python3 bench.py --write-traffic-record {fetch_csv} {write_csv}",
+        ],
+    }
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,7 +479,16 @@ def main():
     ap.add_argument("--n-sweep", action="store_true",
                     help="only run fused and unfused once each at B=1 H=32 d=128 for N = 1k..16k "
                          "(for HBM byte counters), plus the copy calibration")
+    ap.add_argument("--write-traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="host only: write the headline kernel's HBM byte record from two rocprofv3 "
+                         "counter CSVs (FETCH_SIZE, WRITE_SIZE) of `--quick --calibrate-copy` runs")
     args = ap.parse_args()
+
+    if args.write_traffic_record:
+        rec = write_traffic_record(*args.write_traffic_record)
+        print(json.dumps({k: rec[k] for k in ("kernel", "read_bytes_per_launch", "write_bytes_per_launch",
+                                              "bytes_per_launch", "fetch_scale", "write_scale")}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the kernel on one GPU's share of the work); "
@@ -482,7 +554,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "traffic_source": traffic_src,
-                     "kernel": "attn::fwd_bf16::kernel<128, false, 8, 64, true>",
+                     "kernel": HEADLINE_KERNEL,
                      "avg_launch_ms": round(launch_ms, 4),
                      "flop_per_launch": w.flops},
     }

@@ -38,6 +38,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace attn {
@@ -51,6 +52,9 @@ struct Params {
     int nqb;           // query blocks per slice
     float scale_log2;  // scale * log2(e)
     int paired;        // causal: each workgroup runs blocks nqb-1-i and i
+    int BH;            // slices (persistent kernel)
+    int groups;        // workgroup groups, one per XCD (persistent kernel)
+    int per_group;     // workgroups per group (persistent kernel)
 };
 
 template <int D, int WAVES, int BC_>
@@ -370,6 +374,288 @@ void kernel(Params p) {
     }
 }
 
+// Persistent form of the 8-wave K-ahead kernel: one workgroup per CU walks a
+// fixed list of (slice, query block) items and, during the last key tile of
+// one item, already loads the next item's Q rows (into the registers the
+// finished score products no longer need) and its first K and V tiles (into
+// the LDS buffers the last tile no longer reads).  The next item then starts
+// computing at once instead of waiting for those loads with nothing else to
+// do, and the per-workgroup launch disappears.  Each item is computed exactly
+// as the non-persistent kernel computes it (same tiles, same order, same
+// arithmetic), so the results are identical bit for bit.
+//
+// Work assignment.  The grid is groups x per_group workgroups; workgroup w
+// belongs to group w % groups (the dispatcher hands workgroup w to XCD
+// w % groups, so one group is one XCD and shares its L2) at position
+// w / groups.  Group g owns the slices g, g + groups, ... (BH % groups == 0).
+// Its items run slice by slice, item k = (slice k / nqb, block k % nqb), so
+// the per_group workgroups of one round (items r * per_group ..
+// + per_group - 1) read the same key tiles at about the same time.  Causal
+// blocks run longest first within a slice (block nqb-1 - k % nqb), and odd
+// rounds are dealt in reverse, so a workgroup that drew a long block draws a
+// short one next and every workgroup carries about the same number of tiles.
+// (Measured on causal 32k, Q x8: dealing the group's slices side by side,
+// heaviest blocks first, was 2 % slower; not reversing odd rounds, 11 %.)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void persistent_kernel(Params p) {
+    constexpr int WAVES = 8, BC = 64;
+    using T = Tile<D, WAVES, BC>;
+    using L = Layout<D>;
+    constexpr int BR = T::BR, NB = T::NB;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[T::LDS_ELEMS];
+    uint16_t *const Kbuf = smem;                // [2][TILE]
+    uint16_t *const Vbuf = smem + 2 * T::TILE;  // [2][TILE]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases in SGPRs
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const int N = p.N;
+    const int grp = blockIdx.x % p.groups, pos = blockIdx.x / p.groups;
+    const int nsl = p.BH / p.groups;
+    const int nitems = nsl * p.nqb;
+    // (slice, query block) of this workgroup's item in round r; false past the end.
+    auto item_of = [&](int r, int &bh, int &qb) __attribute__((always_inline)) {
+        const int k = r * p.per_group + ((CAUSAL && (r & 1)) ? p.per_group - 1 - pos : pos);
+        if (k >= nitems) return false;
+        const int sl = k / p.nqb;
+        qb = k - sl * p.nqb;
+        if (CAUSAL) qb = p.nqb - 1 - qb;
+        bh = grp + sl * p.groups;
+        return true;
+    };
+
+    uint32_t k_off[T::LOADS_PER_WAVE], v_off[T::LOADS_PER_WAVE];
+#pragma unroll
+    for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
+        const int c = (wave + WAVES * n) * 64 + lane;
+        k_off[n] = L::k_src(c);
+        v_off[n] = L::v_src(c);
+    }
+    const uint32_t slice_bytes = (uint32_t)N * D * 2u;
+    auto rsrc = [&](const uint16_t *base, int bh) __attribute__((always_inline)) {
+        return make_rsrc(base + (size_t)bh * N * D, slice_bytes);
+    };
+    auto load_k = [&](__amdgpu_buffer_rsrc_t r, int tile, int buf) __attribute__((always_inline)) {
+        const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
+#pragma unroll
+        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+            buf_load16_lds_so(r, k_off[n], base, Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+    };
+    auto load_v = [&](__amdgpu_buffer_rsrc_t r, int tile, int buf) __attribute__((always_inline)) {
+        const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
+#pragma unroll
+        for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+            buf_load16_lds_so(r, v_off[n], base, Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+    };
+    // Q fragment (B operand of S^T = K Q^T): lane holds query row qrow and head
+    // dims 16*s + 8*hf .. +7 for each 16-wide step s.  Rows >= N read as zero.
+    bf16x8 qf[D / 16];
+    auto load_q = [&](__amdgpu_buffer_rsrc_t r, int qrow) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+            qf[s] = __builtin_bit_cast(bf16x8, buf_load16(r, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
+    };
+    auto tiles_of = [&](int qb, int &ntiles, int &nfull) __attribute__((always_inline)) {
+        const int r0 = qb * BR;
+        ntiles = (N + BC - 1) / BC;
+        nfull = N / BC;
+        if (CAUSAL) {
+            ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
+            nfull = min(nfull, (r0 + 1) / BC);
+        }
+    };
+
+    int round = 0, bh, qb;
+    if (!item_of(0, bh, qb)) return;
+    {
+        int nt, nf;
+        tiles_of(qb, nt, nf);
+        const auto rk = rsrc(p.k, bh);
+        load_q(rsrc(p.q, bh), qb * BR + wave * 32 + l32);
+        load_k(rk, 0, 0);
+        load_v(rsrc(p.v, bh), 0, 0);
+        if (nt > 1) load_k(rk, 1, 1);
+    }
+    bool v0_late = false;  // the next item's V tile 0 was loaded after the last barrier
+    for (;;) {
+        const auto rk = rsrc(p.k, bh);
+        const auto rv = rsrc(p.v, bh);
+        const int r0 = qb * BR;
+        const int q0 = r0 + wave * 32;
+        const int qrow = q0 + l32;
+        int ntiles, nfull;
+        tiles_of(qb, ntiles, nfull);
+        int nbh = 0, nqb = 0;
+        const bool has_next = item_of(round + 1, nbh, nqb);
+
+        // S^T = K_tile Q^T, one 32x32 accumulator per 32-key block.
+        auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
+            const uint16_t *Ks = Kbuf + buf * T::TILE;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    s[b] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, b, lane)), qf[st], s[b]);
+            }
+        };
+        auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
+        auto v_operand = [&](const uint16_t *Vs, int st, int t) __attribute__((always_inline)) {
+            const i16x4 lo = lds_read_tr16(Vs + L::v_read(st, t, 0, lane));
+            const i16x4 hi = lds_read_tr16(Vs + L::v_read(st, t, 1, lane));
+            const i16x4 w[2] = {lo, hi};
+            return __builtin_bit_cast(bf16x8, w);
+        };
+
+        const float c = p.scale_log2;
+        float m_run = -INFINITY;
+        float l_run = 0.f;
+        f32x16 acc[D / 32];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+        auto softmax = [&](int j, f32x16 (&s)[NB], bf16x8 (&pb)[2 * NB], bool masked) __attribute__((always_inline)) {
+            if (masked) {
+                const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (kk > lim) s[b][r] = -INFINITY;
+                    }
+                }
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = (b == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+            mx = pair_max(mx) * c;
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyThreshold) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run - m_safe);
+                m_run = m_safe;
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+            }
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                u32x4 w[2];
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(fmaf(s[b][r], c, -m_run));
+                    const float p1 = fast_exp2(fmaf(s[b][r + 1], c, -m_run));
+                    w[r >> 3][(r & 7) >> 1] = pack_sum_bf16x2(p0, p1, (r & 2) ? rs1 : rs0);
+                }
+                pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
+                pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
+            }
+            l_run += rs0 + rs1;
+        };
+        auto pv = [&](int buf, const bf16x8 (&pb)[2 * NB]) __attribute__((always_inline)) {
+            const uint16_t *Vs = Vbuf + buf * T::TILE;
+            constexpr int TB = D / 32, NOPS = (BC / 16) * TB, DEPTH = 3;
+            bf16x8 vo[DEPTH];
+#pragma unroll
+            for (int i = 0; i < DEPTH - 1; ++i) vo[i] = v_operand(Vs, i / TB, i % TB);
+#pragma unroll
+            for (int i = 0; i < NOPS; ++i) {
+                const int nx = i + DEPTH - 1;
+                if (nx < NOPS) vo[nx % DEPTH] = v_operand(Vs, nx / TB, nx % TB);
+                acc[i % TB] = mfma32(vo[i % DEPTH], pb[i / TB], acc[i % TB]);
+            }
+        };
+
+        // This item's Q, K(0), V(0) and K(1) were loaded by the previous item's
+        // last step (or before the loop); the barrier there made them visible,
+        // except a V(0) loaded after it.
+        if (round == 0 || v0_late) {
+            wait_vmem();
+            __syncthreads();
+        }
+        f32x16 sa[NB], sb[NB];
+        if (active(0)) scores(0, sa);
+        // The first step refills K buffer 0 (tile 2); every wave must have
+        // finished reading tile 0 from it first.
+        __syncthreads();
+        // During step v the LDS holds K(v+1) and V(v) (buffers (v+1) & 1 and
+        // v & 1); K(v+2) and V(v+1) are in flight.  In the last step the loads
+        // are the next item's: Q (the score products are done with qf), K(0)
+        // and K(1) (no K buffer is read any more) and, when V(v) sits in
+        // buffer 1, V(0).
+        v0_late = false;
+        auto step = [&](int v, f32x16 (&cur)[NB], f32x16 (&nxt)[NB], auto checked) __attribute__((always_inline)) {
+            constexpr bool CHECKED = decltype(checked)::value;
+            if (!CHECKED || v + 2 < ntiles) load_k(rk, v + 2, v & 1);
+            if (!CHECKED || v + 1 < ntiles) {
+                load_v(rv, v + 1, (v + 1) & 1);
+                if (!CHECKED || active(v + 1)) scores((v + 1) & 1, nxt);
+            } else if (has_next) {
+                int nt, nf;
+                tiles_of(nqb, nt, nf);
+                const auto nrk = rsrc(p.k, nbh);
+                load_q(rsrc(p.q, nbh), nqb * BR + wave * 32 + l32);
+                load_k(nrk, 0, 0);
+                if (nt > 1) load_k(nrk, 1, 1);
+                if (v & 1) load_v(rsrc(p.v, nbh), 0, 0);
+                else v0_late = true;
+            }
+            if (!CHECKED || active(v)) {
+                bf16x8 pb[2 * NB];
+                softmax(v, cur, pb, CHECKED && v >= nfull);
+                pv(v & 1, pb);
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        // Unchecked steps: this visit's and the next visit's tiles need no
+        // mask and are visited by every wave, and the loads stay in range.
+        // Steps whose tiles v and v+1 both lie below nfull need no mask and are
+        // visited by every wave: they run without per-tile checks.
+        int v = 0;
+        for (; v + 2 < nfull; v += 2) {
+            step(v, sa, sb, std::false_type{});
+            step(v + 1, sb, sa, std::false_type{});
+        }
+        for (; v + 1 < ntiles; v += 2) {
+            step(v, sa, sb, std::true_type{});
+            step(v + 1, sb, sa, std::true_type{});
+        }
+        if (v < ntiles) step(v, sa, sb, std::true_type{});
+        if (v0_late) load_v(rsrc(p.v, nbh), 0, 0);  // the next item's V(0): buffer 0 is free now
+
+        // Epilogue: O = acc / l, lse = ln(2) * (m + log2 l).
+        const float l_tot = pair_sum(l_run);
+        const float inv = 1.f / l_tot;
+        if (qrow < N) {
+            const auto ro = make_rsrc(p.o + (size_t)bh * N * D, slice_bytes);
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
+                    w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
+                    buf_store8(w, ro, (uint32_t)(qrow * D + 32 * t + 8 * g + 4 * hf) * 2u);
+                }
+            }
+            if (hf == 0 && p.lse) p.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
+        if (!has_next) break;
+        ++round;
+        bh = nbh;
+        qb = nqb;
+    }
+}
+
 // Small grids (fewer query blocks than CUs): the SW waves of a workgroup
 // share one block of 32*RB query rows and split its keys, wave w taking key
 // tiles w, w+SW, w+2*SW, ...  Each wave streams its tiles through its own
@@ -624,6 +910,34 @@ hipError_t launch_split(const FwdArgs &a, hipStream_t s) {
     return launch_split_shape<D, CAUSAL, 4, 1>(a, s);
 }
 
+// The persistent 8-wave kernel: one workgroup per CU, grouped by XCD.  Used
+// when the slices split evenly over the XCDs; false otherwise (the caller then
+// launches the non-persistent kernel).
+template <int D, bool CAUSAL>
+bool launch_persistent(const FwdArgs &a, hipStream_t s, hipError_t &err) {
+    const DeviceShape shape = device_shape();
+    const int groups = shape.xcds;
+    if (a.BH % groups != 0) return false;
+    Params p;
+    p.q = static_cast<const uint16_t *>(a.q);
+    p.k = static_cast<const uint16_t *>(a.k);
+    p.v = static_cast<const uint16_t *>(a.v);
+    p.o = static_cast<uint16_t *>(a.o);
+    p.lse = a.lse;
+    p.N = a.N;
+    p.nqb = (a.N + 255) / 256;
+    p.scale_log2 = a.scale * kLog2e;
+    p.paired = 0;
+    p.BH = a.BH;
+    p.groups = groups;
+    const long long items_per_group = (long long)(a.BH / groups) * p.nqb;
+    p.per_group = (int)std::min<long long>(shape.cus / groups, items_per_group);
+    const unsigned blocks = (unsigned)(groups * p.per_group);
+    hipLaunchKernelGGL((persistent_kernel<D, CAUSAL>), dim3(blocks), dim3(512), 0, s, p);
+    err = hipGetLastError();
+    return true;
+}
+
 template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
 hipError_t launch(const FwdArgs &a, hipStream_t s) {
     using T = Tile<D, WAVES, BC>;
@@ -664,8 +978,15 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
     const bool wide = blocks8 >= 192 && !(CAUSAL && a.N <= 1024);
     if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
-    if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
-    else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
+    if constexpr (CAUSAL) {
+        hipError_t e;
+        if (launch_persistent<D, true>(a, s, e)) return e;
+        return launch<D, CAUSAL, 8, 64, true>(a, s);
+    } else {
+        hipError_t e;
+        if (launch_persistent<D, false>(a, s, e)) return e;
+        return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
+    }
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {

@@ -292,7 +292,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.nqb = (a.N + BR - 1) / BR;
     p.scale_log2 = a.scale * kLog2e;
     const long long blocks = (long long)a.BH * p.nqb;
-    if (blocks < kComputeUnits) {
+    if (blocks < device_shape().cus) {
         // Fewer workgroups than compute units: four times as many, each
         // splitting its keys over its waves.
         p.nqb = (a.N + 31) / 32;

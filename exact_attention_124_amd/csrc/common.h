@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -68,6 +70,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds_wave_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, off,
                                              0, 0, 0);
+}
+
+// The same with the tile's byte offset in the scalar soffset operand, so that
+// a loop over tiles needs no per-lane address arithmetic (voff stays fixed).
+__device__ __forceinline__ void buf_load16_lds_so(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                  void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff,
+                                             soff, 0, 0);
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives element
@@ -142,9 +152,30 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // per workgroup costs more than pairing saves (measured +0.2 to +1.7 % at
 // sixteen rounds, -10 to -17 % at four).  Unpaired grids run one block per
 // workgroup, longest first.
-constexpr int kComputeUnits = 256;  // MI355X
+// Compute units and L2 domains (XCDs) of the current device, read once per
+// device.  gfx950 groups 32 CUs per XCD; a partitioned device (fewer CUs)
+// reports fewer XCDs.  The dispatcher hands workgroup i to XCD i % xcds.
+struct DeviceShape {
+    int cus;
+    int xcds;
+};
+inline DeviceShape device_shape() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];  // cus + 1, 0 = not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+    int cus = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) - 1 : -1;
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        if (dev >= 0) cache[dev].store(cus + 1, std::memory_order_relaxed);
+    }
+    const int xcds = (cus % 32 == 0 && cus >= 32) ? cus / 32 : 1;
+    return DeviceShape{cus, xcds};
+}
 inline bool pair_causal_blocks(long long workgroups, int resident_per_cu) {
-    const long long round = (long long)kComputeUnits * resident_per_cu;
+    const long long round = (long long)device_shape().cus * resident_per_cu;
     return workgroups >= 2 * round && workgroups <= 8 * round;
 }
 

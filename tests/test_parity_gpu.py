@@ -447,3 +447,27 @@ def test_schedule_independence(ea, W):
             assert d_o.max().item() <= BF16_MAX and d_o.mean().item() <= BF16_MEAN and d_l <= 2 * BF16_LSE
         del q, k, v, o_all, l_all
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1500, 2304, 4100])
+def test_persistent_matches_per_block_kernel(ea, W, oracle_mod, causal, N):
+    # With the (batch, head) slices a multiple of the XCD count, the 8-wave
+    # forward runs persistently (one workgroup per CU walking a list of query
+    # blocks, prefetching the next block's Q, K and V); with one slice fewer it
+    # launches one workgroup per query block.  Each block is computed the same
+    # way in both, so shared slices must agree bit for bit.  N = 4100 gives
+    # causal blocks an odd tile count (the next block's first V tile is then
+    # loaded after the last barrier), 1500 and 4100 end in a ragged tile.
+    B, H, d = 1, 64, 128
+    q, k, v = (t.cuda() for t in W.make_qkv(B, H, N, d, torch.bfloat16, seed=1300 + N + causal))
+    say(f"[persistent] B={B} H={H} N={N} causal={causal}")
+    o_all, l_all = ea.attention(q, k, v, causal=causal)
+    o_63, l_63 = ea.attention(q[:, :63].contiguous(), k[:, :63].contiguous(), v[:, :63].contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[:, :63], o_63) and torch.equal(l_all[:, :63], l_63)
+    rows = sorted({0, 255, 256, N // 2, N - 65, N - 1})
+    ro, rl = oracle_mod.attention(q[0, 60:].cpu(), k[0, 60:].cpu(), v[0, 60:].cpu(), 1 / math.sqrt(d), causal,
+                                  rows=rows)
+    rw = torch.tensor(rows, device=o_all.device)
+    check_bf16(o_all[0, 60:][:, rw], l_all[0, 60:][:, rw], ro, rl, "persistent, last slices")
