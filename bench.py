@@ -125,6 +125,35 @@ def time_graph(fn, calls, replays):
     return ms
 
 
+def bench_fused_back_to_back(ea, w, calls=200):
+    """GPU time per call for `calls` binding calls issued back to back
+    between two events (no event pair around each call, no graph): if the
+    binding's host time per call is below the kernel's, the queue never runs
+    dry and this is the kernel's own rate."""
+    import torch
+    from exact_attention_124_amd.workloads import workload_inputs
+    q, k, v = workload_inputs(w, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fn = getattr(ea, "attn_fwd" if w.dtype == torch.bfloat16 else "attn_fwd_f32")
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        fn(q, k, v, o, lse, causal=w.causal, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(calls):
+        fn(q, k, v, o, lse, causal=w.causal, stream=stream)
+    b.record(stream)
+    host_us = (time.perf_counter() - t0) / calls * 1e6
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / calls
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return ms, host_us
+
+
 def bench_fused_graph(ea, w, calls=20, replays=5):
     import torch
     from exact_attention_124_amd.workloads import workload_inputs
@@ -575,8 +604,11 @@ def main():
                           "TFLOP/s": round(ww.flops / (lm * 1e-3) / 1e12, 2),
                           "frac_bf16_peak": round(ww.flops / (lm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
             if gm is not None:
+                bm, host_us = bench_fused_back_to_back(ea, ww)
                 sweep[-1].update({"graph_ms_per_call": round(gm, 4),
-                                  "graph_TFLOP/s": round(ww.flops / (gm * 1e-3) / 1e12, 2)})
+                                  "graph_TFLOP/s": round(ww.flops / (gm * 1e-3) / 1e12, 2),
+                                  "back_to_back_ms_per_call": round(bm, 4),
+                                  "binding_host_us_per_call": round(host_us, 2)})
             if name in ("gpt2_heads_bf16", "causal_2k_bf16"):
                 cm = bench_fused_cold(ea, ww)
                 sweep[-1].update({"cold_launch_ms": round(cm, 4),

@@ -50,6 +50,7 @@ struct Params {
     float scale;
     float scale_log2;   // scale * log2(e)
     int paired;         // causal: each workgroup runs blocks i and nblk-1-i
+    int xcds;           // L2 domains of the device (block remap)
 };
 
 // Tiles read both row-wise (ds_read_b128 of one 16-byte chunk of 16
@@ -180,7 +181,7 @@ void dkdv_kernel(Params p) {
     // workgroup gets the same number of tiles.  Unpaired: one block, in
     // ascending order, which is longest first.
     const bool paired = CAUSAL && p.paired != 0;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int per = paired ? (p.nblk + 1) / 2 : p.nblk;  // workgroups per slice
     const int bh = logical / per;
     const int item = logical - bh * per;
@@ -362,7 +363,7 @@ void dq_kernel(Params p) {
     // Causal: paired (query blocks nblk-1-item, then item) or one block,
     // longest first, as in the forward.
     const bool paired = CAUSAL && p.paired != 0;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int per = paired ? (p.nblk + 1) / 2 : p.nblk;  // workgroups per slice
     const int bh = logical / per;
     const int item = logical - bh * per;
@@ -500,6 +501,7 @@ hipError_t launch(const BwdArgs &a, hipStream_t s) {
     p.N = a.N;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
+    p.xcds = device_shape().xcds;
     const long long prows = (long long)a.BH * p.Npad;
     hipLaunchKernelGGL((stats_kernel<D>), dim3((unsigned)((prows + 15) / 16)), dim3(256), 0, s, p.o, p.dout,
                        p.lse, p.stats, a.N, p.Npad, prows, a.scale);

@@ -55,6 +55,7 @@ struct Params {
     int BH;            // slices (persistent kernel)
     int groups;        // workgroup groups, one per XCD (persistent kernel)
     int per_group;     // workgroups per group (persistent kernel)
+    int xcds;          // L2 domains of the device (block remap)
 };
 
 template <int D, int WAVES, int BC_>
@@ -124,7 +125,7 @@ void kernel(Params p) {
     // after the other, so every workgroup gets the same number of tiles and no
     // long block starts last.  Causal, unpaired: one block, longest first.
     const bool paired = CAUSAL && p.paired != 0;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int per = paired ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
     const int bh = logical / per;
     const int item = logical - bh * per;
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(64 * SW) void split_kernel(Params p) {
     uint16_t *const Kw = smem + wave * WREG;  // [2][TILE]
     uint16_t *const Vw = Kw + 2 * TILE;       // [2][TILE]
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int bh = logical / p.nqb;
     int qb = logical - bh * p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;  // longest rows first
@@ -891,6 +892,7 @@ hipError_t launch_split_shape(const FwdArgs &a, hipStream_t s) {
     p.nqb = (a.N + 32 * RB - 1) / (32 * RB);
     p.scale_log2 = a.scale * kLog2e;
     p.paired = 0;
+    p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.BH * (unsigned)p.nqb;
     hipLaunchKernelGGL((split_kernel<D, CAUSAL, SW, RB>), dim3(blocks), dim3(64 * SW), 0, s, p);
     return hipGetLastError();
@@ -930,6 +932,7 @@ bool launch_persistent(const FwdArgs &a, hipStream_t s, hipError_t &err) {
     p.paired = 0;
     p.BH = a.BH;
     p.groups = groups;
+    p.xcds = groups;
     const long long items_per_group = (long long)(a.BH / groups) * p.nqb;
     p.per_group = (int)std::min<long long>(shape.cus / groups, items_per_group);
     const unsigned blocks = (unsigned)(groups * p.per_group);
@@ -951,6 +954,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.nqb = (a.N + T::BR - 1) / T::BR;
     p.scale_log2 = a.scale * kLog2e;
     p.paired = CAUSAL && pair_causal_blocks((long long)a.BH * p.nqb, WAVES == 8 ? 1 : 2);
+    p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
     hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();

@@ -24,6 +24,7 @@ struct Params {
     int N;
     int nqb;
     float scale_log2;
+    int xcds;  // L2 domains of the device (block remap)
 };
 
 constexpr int BR = 128;  // query rows per workgroup
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) float Ks[BC * STR];
     __shared__ __attribute__((aligned(16))) float Vs[BC * STR];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int bh = logical / p.nqb;
     int qb = logical - bh * p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
@@ -179,12 +180,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(Params p) {
 
 // Split-key variant for grids too small to occupy the chip: a workgroup owns
 // 32 query rows and its four waves take the four 32-key quarters of each
-// 128-key step, each keeping its own running state.  At the end the four
-// states of a row are merged -- the maximum of the four maxima, each sum and
-// output scaled by 2^(m_w - m) before adding -- which gives the same result as
-// one pass over all keys ("The Attention Bottleneck -- and How FlashAttention
-// Fixed It", section "Online softmax": partial softmax states over disjoint key
-// sets combine exactly under a common maximum).
+// 128-key step, each keeping its own running state (the running
+// normalisation of "The Attention Bottleneck -- and How FlashAttention Fixed
+// It", section "The fix: tiling and fusion, never touch HBM").  At the end the
+// four states of a row are merged under their common maximum,
+//     m = max_w m_w,  l = sum_w 2^(m_w - m) l_w,  O = sum_w 2^(m_w - m) O_w / l,
+// which gives the same result as one pass over all keys up to rounding: each
+// state's sum and output were accumulated relative to its own m_w, and the
+// factor 2^(m_w - m) moves them to the common reference.  (The pages do not
+// state this merge; it follows from the definition of the softmax.)
 constexpr int SPLIT = 4;  // waves per query block, one per key quarter
 
 template <int D, bool CAUSAL>
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_split_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) float Ks[STEP * STR];
     __shared__ __attribute__((aligned(16))) float Vs[STEP * STR];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int bh = logical / p.nqb;
     int qb = logical - bh * p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
@@ -291,8 +295,10 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.N = a.N;
     p.nqb = (a.N + BR - 1) / BR;
     p.scale_log2 = a.scale * kLog2e;
+    const DeviceShape shape = device_shape();
+    p.xcds = shape.xcds;
     const long long blocks = (long long)a.BH * p.nqb;
-    if (blocks < device_shape().cus) {
+    if (blocks < shape.cus) {
         // Fewer workgroups than compute units: four times as many, each
         // splitting its keys over its waves.
         p.nqb = (a.N + 31) / 32;

@@ -73,6 +73,7 @@ struct Params {
     float scale_log2;  // scale * q_descale * k_descale * log2(e)
     float v_descale;
     int paired;        // causal: each workgroup runs blocks nqb-1-i and i
+    int xcds;          // L2 domains of the device (block remap)
 };
 
 template <int D, int WAVES, int BC_>
@@ -147,7 +148,7 @@ void kernel(Params p) {
     // Causal: paired (blocks nqb-1-item, then item) or one block, longest
     // first, as in the bf16 kernel.
     const bool paired = CAUSAL && p.paired != 0;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int per = paired ? (p.nqb + 1) / 2 : p.nqb;  // workgroups per slice
     const int bh = logical / per;
     const int item = logical - bh * per;
@@ -373,6 +374,7 @@ hipError_t launch(const Fp8Args &a, hipStream_t s) {
     p.scale_log2 = a.f.scale * a.q_descale * a.k_descale * kLog2e;
     p.v_descale = a.v_descale;
     p.paired = CAUSAL && pair_causal_blocks((long long)a.f.BH * p.nqb, WAVES == 8 ? 1 : 2);
+    p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.f.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
     hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();

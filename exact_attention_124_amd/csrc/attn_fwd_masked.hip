@@ -49,6 +49,7 @@ struct Params {
     int nqb;
     int wl, wr;  // window sides, < 0 = unbounded
     float scale;
+    int xcds;    // L2 domains of the device (block remap)
 };
 
 constexpr int WAVES = 4, BC = 64;
@@ -64,7 +65,7 @@ void kernel(Params p) {
     uint16_t *const Kbuf = smem;
     uint16_t *const Vbuf = smem + 2 * T::TILE;
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, p.xcds);
     const int bh = logical / p.nqb;
     int qb = logical - bh * p.nqb;
     if (CAUSAL) qb = p.nqb - 1 - qb;
@@ -317,6 +318,7 @@ hipError_t launch(const MaskedArgs &a, hipStream_t s) {
     p.wl = a.window_left;
     p.wr = a.window_right;
     p.scale = a.f.scale;
+    p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.f.BH * (unsigned)p.nqb;
     hipLaunchKernelGGL((kernel<D, CAUSAL, BIAS, WINDOW>), dim3(blocks), dim3(64 * WAVES), 0, s, p);
     return hipGetLastError();

@@ -30,13 +30,13 @@ template <int D, bool VEC>
 __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t *__restrict__ Q,
                                                           const uint16_t *__restrict__ K,
                                                           uint16_t *__restrict__ S, int N, int nqb,
-                                                          int nkb) {
+                                                          int nkb, int xcds) {
     constexpr int KSTR = D + 8;
     constexpr int SSTR = 128 + 8;
     constexpr int LDS_ELEMS = (128 * KSTR > 128 * SSTR) ? 128 * KSTR : 128 * SSTR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, xcds);
     const int kb = logical % nkb;
     const int rest = logical / nkb;
     const int qb = rest % nqb;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void softmax_rows_bf16_stream_kernel(uint16_t 
 
 template <int D>
 __global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,
-                                                      uint16_t *__restrict__ O, int N, int nqb) {
+                                                      uint16_t *__restrict__ O, int N, int nqb, int xcds) {
     using VL = fwd_bf16::Layout<D>;
     constexpr int WAVES = 8, BK = 64, STAGES = 3;
     constexpr int BR = 32 * WAVES;            // query rows per workgroup
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict
     static_assert(PLW * WAVES * 1024 == PT * 2 && VLW * WAVES * 1024 == VT * 2, "tile loads must split evenly");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * SLOT];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, xcds);
     const int bh = logical / nqb;
     const int qb = logical - bh * nqb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -359,14 +359,14 @@ __global__ __launch_bounds__(512) void pv_ring_kernel(const uint16_t *__restrict
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pv_bf16_kernel(const uint16_t *__restrict__ P, const uint16_t *__restrict__ V,
-                    uint16_t *__restrict__ O, int N, int nqb) {
+                    uint16_t *__restrict__ O, int N, int nqb, int xcds) {
     constexpr int BC = 64;
     constexpr int VSTR = BC + 8;
     constexpr int VBUF = D * VSTR;
     constexpr int VITEMS = (BC / 4) * (D / 8);
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * VBUF];
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int logical = xcd_remap(blockIdx.x, gridDim.x, xcds);
     const int bh = logical / nqb;
     const int qb = logical - bh * nqb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -551,11 +551,12 @@ hipError_t launch_bf16(const FwdArgs &a, void *ws, hipStream_t s) {
     const auto *v = static_cast<const uint16_t *>(a.v);
     auto *o = static_cast<uint16_t *>(a.o);
     auto *S = static_cast<uint16_t *>(ws);
+    const int xcds = device_shape().xcds;
     const unsigned g1 = (unsigned)a.BH * (unsigned)nqb * (unsigned)nqb;
     if (vec)
-        hipLaunchKernelGGL((scores_bf16_kernel<D, true>), dim3(g1), dim3(256), 0, s, q, k, S, N, nqb, nqb);
+        hipLaunchKernelGGL((scores_bf16_kernel<D, true>), dim3(g1), dim3(256), 0, s, q, k, S, N, nqb, nqb, xcds);
     else
-        hipLaunchKernelGGL((scores_bf16_kernel<D, false>), dim3(g1), dim3(256), 0, s, q, k, S, N, nqb, nqb);
+        hipLaunchKernelGGL((scores_bf16_kernel<D, false>), dim3(g1), dim3(256), 0, s, q, k, S, N, nqb, nqb, xcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -583,9 +584,9 @@ hipError_t launch_bf16(const FwdArgs &a, void *ws, hipStream_t s) {
     const unsigned g3 = (unsigned)a.BH * (unsigned)nqb;
     const int nqr = (N + 255) / 256;
     if (vec)
-        hipLaunchKernelGGL((pv_ring_kernel<D>), dim3((unsigned)a.BH * (unsigned)nqr), dim3(512), 0, s, S, v, o, N, nqr);
+        hipLaunchKernelGGL((pv_ring_kernel<D>), dim3((unsigned)a.BH * (unsigned)nqr), dim3(512), 0, s, S, v, o, N, nqr, xcds);
     else
-        hipLaunchKernelGGL((pv_bf16_kernel<D>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb);
+        hipLaunchKernelGGL((pv_bf16_kernel<D>), dim3(g3), dim3(256), 0, s, S, v, o, N, nqb, xcds);
     return hipGetLastError();
 }
 

@@ -180,13 +180,14 @@ inline bool pair_causal_blocks(long long workgroups, int resident_per_cu) {
 }
 
 // Block index remap so that consecutive logical blocks land on the same XCD.
-// The dispatcher hands workgroup i to XCD (i % 8); this inverts that so the
-// blocks of one attention head share one XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    const int xcd = bid & 7;
-    const int local = bid >> 3;
-    const int per = nblocks >> 3;
-    const int rem = nblocks & 7;
+// The dispatcher hands workgroup i to XCD (i % xcds); this inverts that so the
+// blocks of one attention head share one XCD's L2.  A bijection of
+// [0, nblocks) for any xcds >= 1 (so a wrong count costs locality only).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks, int xcds) {
+    const int xcd = bid % xcds;
+    const int local = bid / xcds;
+    const int per = nblocks / xcds;
+    const int rem = nblocks - per * xcds;
     const int start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
     return start + local;
 }
