@@ -163,7 +163,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const uint16_t *__restrict__
 
 // ---------------------------------------------------------------------------
 // 2. dK, dV.  WAVES waves x 32 keys; BQ-query tiles of Q and dO stream
-//    through double-buffered LDS.
+//    through double-buffered LDS.  K stays in VGPRs (B operand of S = Q K^T);
+//    the workgroup's V rows sit in LDS (B operand of dP = dO V^T), which
+//    leaves the register room for the 128 accumulator registers of dK and dV
+//    without spilling.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int WAVES, int BQ, int OCC>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
@@ -172,7 +175,13 @@ void dkdv_kernel(Params p) {
     constexpr int QT = BQ * D;                       // elements per Q or dO tile
     constexpr int LPW = QT / 512 / WAVES;            // wave-loads per wave per tile
     static_assert(LPW >= 1 && (QT / 512) % WAVES == 0, "tile loads must split evenly");
+    constexpr int VLW = BK * D / 512 / WAVES;        // wave-loads per wave of the V rows
+    static_assert(VLW >= 1 && (BK * D / 512) % WAVES == 0, "V loads must split evenly");
+    constexpr int SLW = 2 * BQ / 64;                 // 4-byte wave-loads of one tile's statistics
+    static_assert(SLW >= 1 && SLW <= WAVES, "statistics loads: one per wave at most");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * QT];
+    __shared__ __attribute__((aligned(1024))) uint16_t vsm[BK * D];  // V rows of the workgroup's keys
+    __shared__ __attribute__((aligned(16))) float sstat[2][2 * BQ];  // [buf][-lse/scale of BQ rows, then -D]
     uint16_t *const Qbuf = smem;             // [2][QT]
     uint16_t *const Obuf = smem + 2 * QT;    // [2][QT] (dO)
 
@@ -188,13 +197,10 @@ void dkdv_kernel(Params p) {
     const int npass = (paired && p.nblk - 1 - item != item) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
         const int kb = (paired && pass == 1) ? p.nblk - 1 - item : item;
-        // Non-causal: readfirstlane tells the compiler the wave index is uniform,
-        // which makes the edge-tile test a scalar branch that interior tiles
-        // skip.  Causal (where edge tiles are common): left as is, the test is
-        // folded into the probability loop as selects, which keeps fewer values
-        // live than a branch around it and avoids spilling.
+        // readfirstlane: the wave index is uniform, so the edge-tile test below
+        // is a scalar branch that interior tiles skip.
         const int tid = threadIdx.x, lane = tid & 63;
-        const int wave = CAUSAL ? (tid >> 6) : __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int l32 = lane & 31, hf = lane >> 5;
         const int N = p.N;
 
@@ -206,36 +212,57 @@ void dkdv_kernel(Params p) {
         const auto rdo = make_rsrc(p.dout + slice, slice_bytes);
         const auto rdk = make_rsrc(p.dk + slice, slice_bytes);
         const auto rdv = make_rsrc(p.dv + slice, slice_bytes);
+        // Statistics of this slice: [2][Npad] floats.  With 32-query tiles one
+        // wave loads both halves of a tile's block (rows stay below Npad);
+        // with 64-query tiles wave w loads statistic w, each through a
+        // resource of its own half, so rows past Npad read as zero.
         const float *st = p.stats + (size_t)bh * 2 * p.Npad;
-        const auto rlse = make_rsrc(st, (uint32_t)p.Npad * 4u);
-        const auto rdl = make_rsrc(st + p.Npad, (uint32_t)p.Npad * 4u);
+        const auto rst = SLW == 1 ? make_rsrc(st, (uint32_t)p.Npad * 8u)
+                                  : make_rsrc(st + (wave % SLW) * p.Npad, (uint32_t)p.Npad * 4u);
 
         const int k0 = kb * BK + wave * 32;  // first key of this wave
         const int key = k0 + l32;            // this lane's key
 
-        // Resident K and V (B operands of S = Q K^T and dP = dO V^T): lane holds
-        // key `key`, columns 16*st + 8*hf .. +7.  Keys >= N read as zero.
-        bf16x8 kf[D / 16], vf[D / 16];
+        // Resident K: lane holds key `key`, columns 16*st + 8*hf .. +7.  Keys
+        // >= N read as zero.
+        bf16x8 kf[D / 16];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const uint32_t off = (uint32_t)(key * D + 16 * st + 8 * hf) * 2u;
-            kf[st] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-            vf[st] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+        for (int st = 0; st < D / 16; ++st)
+            kf[st] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)(key * D + 16 * st + 8 * hf) * 2u));
+
+        // All direct-to-LDS loads are issued from inline assembly, so that the
+        // compiler does not drain them before every LDS read of the current
+        // tile; each wave waits for its own with wait_vmem before the barrier
+        // that ends the tile.  V rows of the block first (in the tiles' row
+        // layout; rows >= N read as zero); the first tile's barrier covers them.
+        if (pass > 0) __syncthreads();  // every wave is done with the previous block's V
+        {
+            const uint32_t vbase = __builtin_amdgcn_readfirstlane((uint32_t)(kb * BK * D) * 2u);
+#pragma unroll
+            for (int n = 0; n < VLW; ++n)
+                load16_lds_async_so(rv, src_off<D>((wave + WAVES * n) * 64 + lane), vbase,
+                                    vsm + (wave + WAVES * n) * 512);
         }
 
         const int nqt = (N + BQ - 1) / BQ;
         const int t0 = CAUSAL ? (kb * BK) / BQ : 0;  // first query tile that sees any key of the block
-        auto active = [&](int i) __attribute__((always_inline)) { return !CAUSAL || i * BQ + BQ - 1 >= k0; };
 
+        // Q and dO tiles; the statistics of the tile's BQ query rows come with
+        // them, 4 bytes per lane, as a [2][BQ] block (-lse/scale, then -D).
         uint32_t ld_off[LPW];
 #pragma unroll
         for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
         auto load_tile = [&](int i, int buf) __attribute__((always_inline)) {
-            const uint32_t base = (uint32_t)(i * BQ * D) * 2u;
+            if (wave < SLW) {
+                const uint32_t st_off = SLW == 1 ? (uint32_t)(hf * p.Npad + l32) * 4u : (uint32_t)lane * 4u;
+                load4_lds_async_so(rst, st_off, __builtin_amdgcn_readfirstlane((uint32_t)(i * BQ) * 4u),
+                                   &sstat[buf][64 * wave]);
+            }
+            const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(i * BQ * D) * 2u);
 #pragma unroll
             for (int n = 0; n < LPW; ++n) {
-                buf_load16_lds(rq, base + ld_off[n], Qbuf + buf * QT + (wave + WAVES * n) * 512);
-                buf_load16_lds(rdo, base + ld_off[n], Obuf + buf * QT + (wave + WAVES * n) * 512);
+                load16_lds_async_so(rq, ld_off[n], base, Qbuf + buf * QT + (wave + WAVES * n) * 512);
+                load16_lds_async_so(rdo, ld_off[n], base, Obuf + buf * QT + (wave + WAVES * n) * 512);
             }
         };
 
@@ -247,91 +274,86 @@ void dkdv_kernel(Params p) {
             dv[t] = f32x16{};
         }
 
-        if (t0 < nqt) {
-            load_tile(t0, 0);
-            wait_vmem();
-            __syncthreads();
-        }
+        if (t0 < nqt) load_tile(t0, 0);
+        wait_vmem();
+        __syncthreads();
+        // Every tile from t0 on is computed by every wave: a causal wave whose
+        // keys all lie past the tile's last query gets P = 0 from the edge
+        // test (three such tiles at most, for the block's upper waves), which
+        // keeps the loop free of a per-wave skip and its register copies.
         for (int i = t0; i < nqt; ++i) {
             const int buf = (i - t0) & 1;
-            if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
-            if (active(i)) {
-                const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
-                // Accumulator starting values: -lse/scale and -D of this lane's
-                // query rows 32*qb + 8*g + 4*hf + 0..3, four rows per 16-byte load
-                // (within the padded rows, so every load is in range).
-                f32x16 s[NQB], dp[NQB];
+            const uint16_t *Qs = Qbuf + buf * QT, *Os = Obuf + buf * QT;
+            // Accumulator starting values: -lse/scale and -D of this lane's
+            // query rows 32*qb + 8*g + 4*hf + 0..3, four rows per 16-byte LDS
+            // read (rows past N hold the padding zeros).
+            const float *Ss = sstat[buf];
+            f32x16 s[NQB], dp[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                f32x4 a[4], b[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    a[g] = *reinterpret_cast<const f32x4 *>(Ss + 32 * qb + 8 * g + 4 * hf);
+                    b[g] = *reinterpret_cast<const f32x4 *>(Ss + BQ + 32 * qb + 8 * g + 4 * hf);
+                }
+                s[qb] = __builtin_bit_cast(f32x16, a);
+                dp[qb] = __builtin_bit_cast(f32x16, b);
+            }
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    f32x4 a[4], b[4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const uint32_t off = (uint32_t)(i * BQ + 32 * qb + 8 * g + 4 * hf) * 4u;
-                        a[g] = __builtin_bit_cast(f32x4, buf_load16(rlse, off));
-                        b[g] = __builtin_bit_cast(f32x4, buf_load16(rdl, off));
-                    }
-                    s[qb] = __builtin_bit_cast(f32x16, a);
-                    dp[qb] = __builtin_bit_cast(f32x16, b);
+                    s[qb] = mfma32(row_operand<D>(Qs, 32 * qb, st, lane), kf[st], s[qb]);
+                    dp[qb] = mfma32(row_operand<D>(Os, 32 * qb, st, lane), row_operand<D>(vsm, 32 * wave, st, lane),
+                                    dp[qb]);
                 }
+            }
+            // The next tile's loads are issued once S and dP are done: a
+            // vector-memory wait before that point (a register reload) would
+            // otherwise wait for them too.
+            if (i + 1 < nqt) load_tile(i + 1, buf ^ 1);
+            // P = exp2(c S'), dS = P dP'; pairs past the sequence end or above
+            // the causal diagonal get P = 0, in a block of its own that interior
+            // tiles branch around.
+            const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
 #pragma unroll
-                for (int st = 0; st < D / 16; ++st) {
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        s[qb] = mfma32(row_operand<D>(Qs, 32 * qb, st, lane), kf[st], s[qb]);
-                        dp[qb] = mfma32(row_operand<D>(Os, 32 * qb, st, lane), vf[st], dp[qb]);
+                for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(s[qb][r] * c);
+            if (edge) {
+                // Query row of element r of block qb: g0 + cr with g0 = i*BQ +
+                // 4*hf and cr = 32*qb + 8*(r/4) + r%4 a constant, so the tests
+                // row >= N and key > row compare cr against two per-lane values
+                // (kept opaque so that the per-element offsets are not hoisted
+                // out of the loop into registers).
+                const int g0 = i * BQ + 4 * hf;
+                int lim = N - g0, rel = key - g0;
+                asm volatile("" : "+v"(lim), "+v"(rel));
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int cr = 32 * qb + 8 * (r >> 2) + (r & 3);
+                        if (cr >= lim || (CAUSAL && rel > cr)) s[qb][r] = 0.f;
                     }
+            }
+            bf16x8 pb[2 * NQB], db[2 * NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = s[qb][r];
+                    pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
+                    db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
                 }
-                // P = exp2(c S'), dS = P dP'; pairs past the sequence end or above
-                // the causal diagonal get P = 0.  Causal: the test sits inside the
-                // loop (evaluated as selects on every tile, which keeps the fewest
-                // values live); non-causal: only the ragged last tile needs it, in
-                // a block of its own that every other tile branches around.
-                const bool edge = (i * BQ + BQ > N) || (CAUSAL && i * BQ < k0 + 31);
-                bf16x8 pb[2 * NQB], db[2 * NQB];
-                if constexpr (CAUSAL) {
+            // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
+            for (int st = 0; st < BQ / 16; ++st) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            float pr = fast_exp2(s[qb][r] * c);
-                            if (edge) {
-                                const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                                if (qi >= N || key > qi) pr = 0.f;
-                            }
-                            pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
-                            db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
-                        }
-                } else {
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) s[qb][r] = fast_exp2(s[qb][r] * c);
-                    if (edge) {
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int qi = i * BQ + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                                if (qi >= N) s[qb][r] = 0.f;
-                            }
-                    }
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float pr = s[qb][r];
-                            pb[2 * qb + (r >> 3)][r & 7] = (__bf16)pr;
-                            db[2 * qb + (r >> 3)][r & 7] = (__bf16)(pr * dp[qb][r]);
-                        }
-                }
-                // dV^T += dO^T P, dK^T += Q^T dS (scale applied at the end).
-#pragma unroll
-                for (int st = 0; st < BQ / 16; ++st) {
-#pragma unroll
-                    for (int t = 0; t < D / 32; ++t) {
-                        dv[t] = mfma32(tr_operand<D>(Os, st, t, lane), pb[st], dv[t]);
-                        dk[t] = mfma32(tr_operand<D>(Qs, st, t, lane), db[st], dk[t]);
-                    }
+                for (int t = 0; t < D / 32; ++t) {
+                    dv[t] = mfma32(tr_operand<D>(Os, st, t, lane), pb[st], dv[t]);
+                    dk[t] = mfma32(tr_operand<D>(Qs, st, t, lane), db[st], dk[t]);
                 }
             }
             wait_vmem();
@@ -407,15 +429,16 @@ void dq_kernel(Params p) {
         }
         auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
 
+        // Direct-to-LDS tile loads from inline assembly, as in the dK/dV kernel.
         uint32_t ld_off[LPW];
 #pragma unroll
         for (int n = 0; n < LPW; ++n) ld_off[n] = src_off<D>((wave + WAVES * n) * 64 + lane);
         auto load_tile = [&](int j, int buf) __attribute__((always_inline)) {
-            const uint32_t base = (uint32_t)(j * BC * D) * 2u;
+            const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(j * BC * D) * 2u);
 #pragma unroll
             for (int n = 0; n < LPW; ++n) {
-                buf_load16_lds(rk, base + ld_off[n], Kbuf + buf * KT + (wave + WAVES * n) * 512);
-                buf_load16_lds(rv, base + ld_off[n], Vbuf + buf * KT + (wave + WAVES * n) * 512);
+                load16_lds_async_so(rk, ld_off[n], base, Kbuf + buf * KT + (wave + WAVES * n) * 512);
+                load16_lds_async_so(rv, ld_off[n], base, Vbuf + buf * KT + (wave + WAVES * n) * 512);
             }
         };
 

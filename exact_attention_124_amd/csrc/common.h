@@ -118,6 +118,38 @@ __device__ __forceinline__ void load16_lds_async(__amdgpu_buffer_rsrc_t r, uint3
         : "s"(base), "v"(voff), "s"(r)
         : "memory");
 }
+
+// The same with a scalar byte offset (soffset) added to voff, and a 4-byte
+// variant (lane l's 4 bytes land at lds + 4*l), for loops whose per-tile
+// offset is wave-uniform.
+__device__ __forceinline__ void load16_lds_async_so(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                    const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r), "s"(soff)
+        : "memory");
+}
+__device__ __forceinline__ void load4_lds_async_so(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                   const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(base), "v"(voff), "s"(r), "s"(soff)
+        : "memory");
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two floats -> two bf16 (round to nearest even) packed low/high in one word.
