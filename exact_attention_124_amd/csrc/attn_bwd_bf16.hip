@@ -421,13 +421,17 @@ void dq_kernel(Params p) {
         const float nlse2 = live ? stq[qrow] * p.scale_log2 : 0.f;  // -lse * log2(e)
         const float ndlt = live ? stq[p.Npad + qrow] : 0.f;           // -D
 
+        // Key tiles of the block: interior tiles [0, nint) need no mask; the
+        // edge tiles [nint, ntiles) (the ragged end, and for causal blocks the
+        // tiles that reach past the block's first query) run a copy of the loop
+        // body with the mask.  Every wave computes every tile (a causal wave
+        // whose queries all precede a tile's keys gets P = 0 there).
         int ntiles = (N + BC - 1) / BC;
-        int nfull = N / BC;
+        int nint = N / BC;
         if (CAUSAL) {
             ntiles = min(ntiles, (r0 + BR - 1) / BC + 1);
-            nfull = min(nfull, (r0 + 1) / BC);
+            nint = min(nint, (r0 + 1) / BC);
         }
-        auto active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * BC <= q0 + 31; };
 
         // Direct-to-LDS tile loads from inline assembly, as in the dK/dV kernel.
         uint32_t ld_off[LPW];
@@ -443,57 +447,58 @@ void dq_kernel(Params p) {
         };
 
         const float c = p.scale_log2;
+        const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last key this lane's query sees
         f32x16 dq[D / 32];
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) dq[t] = f32x16{};
 
-        load_tile(0, 0);
-        wait_vmem();
-        __syncthreads();
-        for (int j = 0; j < ntiles; ++j) {
+        auto tile = [&](int j, bool masked) __attribute__((always_inline)) {
             const int buf = j & 1;
             if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-            if (active(j)) {
-                const uint16_t *Ks = Kbuf + buf * KT, *Vs = Vbuf + buf * KT;
-                f32x16 s[2], dp[2];
+            const uint16_t *Ks = Kbuf + buf * KT, *Vs = Vbuf + buf * KT;
+            // The tile's two 32-key blocks one after the other (scores, dS,
+            // then their share of the dQ product), which halves the live
+            // score registers.
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    s[b] = f32x16{};
-                    dp[b] = f32x16{};
-                }
+            for (int b = 0; b < 2; ++b) {
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
                 for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        s[b] = mfma32(row_operand<D>(Ks, 32 * b, st, lane), qf[st], s[b]);
-                        dp[b] = mfma32(row_operand<D>(Vs, 32 * b, st, lane), of[st], dp[b]);
-                    }
+                    s = mfma32(row_operand<D>(Ks, 32 * b, st, lane), qf[st], s);
+                    dp = mfma32(row_operand<D>(Vs, 32 * b, st, lane), of[st], dp);
                 }
-                const bool masked = j >= nfull;
-                const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
-                bf16x8 db[4];
+                // dS = P (dP - D) as the bf16 B operand of the dQ product;
+                // masked tiles zero P for keys past `lim`.  Key of element r:
+                // j*BC + 32*b + 8*(r/4) + 4*hf + r%4.
+                bf16x8 db[2];
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float pr = fast_exp2(fmaf(s[b][r], c, nlse2));
-                        if (masked) {
-                            const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            if (kk > lim) pr = 0.f;
-                        }
-                        db[2 * b + (r >> 3)][r & 7] = (__bf16)(pr * (dp[b][r] + ndlt));
+                for (int r = 0; r < 16; ++r) {
+                    float pr = fast_exp2(fmaf(s[r], c, nlse2));
+                    if (masked) {
+                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (kk > lim) pr = 0.f;
                     }
+                    db[r >> 3][r & 7] = (__bf16)(pr * (dp[r] + ndlt));
                 }
-                // dQ^T += K^T dS^T (scale applied at the end).
+                // dQ^T += K^T dS^T over the block's keys (scale applied at the end).
 #pragma unroll
-                for (int st = 0; st < BC / 16; ++st) {
+                for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                    for (int t = 0; t < D / 32; ++t) dq[t] = mfma32(tr_operand<D>(Ks, st, t, lane), db[st], dq[t]);
+                    for (int t = 0; t < D / 32; ++t)
+                        dq[t] = mfma32(tr_operand<D>(Ks, 2 * b + h, t, lane), db[h], dq[t]);
                 }
             }
             wait_vmem();
             __syncthreads();
-        }
+        };
+
+        if (pass > 0) __syncthreads();  // every wave is done with the previous block's tiles
+        load_tile(0, 0);
+        wait_vmem();
+        __syncthreads();
+        int j = 0;
+        for (; j < nint; ++j) tile(j, false);
+        for (; j < ntiles; ++j) tile(j, true);
         if (live) store_rows<D>(dq, p.scale, rdq, qrow, hf);
     }
 }
