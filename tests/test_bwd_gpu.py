@@ -124,6 +124,26 @@ def test_backward_causal_paired_odd_block_count(ea, W, oracle_mod):
     check((flat(dq)[:, idx], flat(dk)[:, idx], flat(dv)[:, idx]), ref, "paired, 17 blocks")
 
 
+@pytest.mark.parametrize("d,N", [(128, 1500), (64, 2100)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_ragged_multiblock(ea, W, oracle_mod, d, N, causal):
+    # Several key and query blocks with a ragged end: the dK/dV kernel's
+    # masked diagonal and tail tiles, its statistics block past N (zeros), and
+    # the dQ kernel's separate interior and edge loops.  Rows and keys at block
+    # and tile boundaries plus a seeded sample, in every slice.
+    B, H = 2, 3
+    q, k, v = W.make_qkv(B, H, N, d, torch.bfloat16, seed=300 + N)
+    g = W.make_grad(B, H, N, d, torch.bfloat16, seed=300 + N)
+    say(f"[bwd] ragged B={B} H={H} N={N} d={d} causal={causal}")
+    dq, dk, dv = gpu_grads(ea, q, k, v, g, causal)
+    edges = [0, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 65, N - 64, N - 33, N - 32, N - 2, N - 1]
+    idx = sorted(set(i for i in edges if 0 <= i < N) | set(W.sample_rows(N, 24, seed=6)))
+    flat = lambda t: t.reshape(-1, N, d)  # noqa: E731
+    ref = oracle_mod.attention_backward(flat(q), flat(k), flat(v), flat(g), 1 / math.sqrt(d), causal,
+                                        rows=idx, keys=idx)
+    check((flat(dq)[:, idx], flat(dk)[:, idx], flat(dv)[:, idx]), ref, f"ragged N={N} d={d}")
+
+
 def test_backward_closed_forms_and_determinism(ea, W):
     q, k, v = (t.cuda() for t in W.make_qkv(2, 4, 700, 128, torch.bfloat16, seed=31))
     g = W.make_grad(2, 4, 700, 128, torch.bfloat16, seed=31).cuda()
