@@ -151,26 +151,21 @@ void kernel(Params p) {
         k_off[n] = L::k_src(c);
         v_off[n] = L::v_src(c);
     }
+    // K/V tile copies go straight to LDS from inline assembly: the compiler
+    // does not see them, so it does not drain them (and, loads completing in
+    // order, the bias reads issued after them) before every LDS read.  Each
+    // wave waits for its own copies before the barrier that ends the tile.
     auto load_kv = [&](int tile, int buf) __attribute__((always_inline)) {
-        const uint32_t base = (uint32_t)(tile * BC * D) * 2u;
+        const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(tile * BC * D) * 2u);
 #pragma unroll
         for (int n = 0; n < T::LOADS_PER_WAVE; ++n) {
-            buf_load16_lds(rk, base + k_off[n], Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
-            buf_load16_lds(rv, base + v_off[n], Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+            load16_lds_async_so(rk, k_off[n], base, Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+            load16_lds_async_so(rv, v_off[n], base, Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
         }
     };
-
-    const float sc = p.scale;
-    const float cu = BIAS != 0 ? kLog2e : sc * kLog2e;
-    float m_run = -INFINITY;  // running reference maximum, log2 units
-    float l_run = 0.f;
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-
-    auto tile_step = [&](int j, int buf) __attribute__((always_inline)) {
-        // Bias of this tile: 4 keys per 16-byte read, in accumulator order.
-        f32x4 bz[NB][4];
+    // Bias of tile j: 4 keys per 16-byte read, in accumulator order.
+    constexpr int BIAS_LOADS = BIAS == 2 ? NB * 4 : BIAS == 1 ? NB * 16 : 0;  // vector loads per tile
+    auto load_bias = [&](int j, f32x4 (&bz)[NB][4]) __attribute__((always_inline)) {
         if constexpr (BIAS) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -187,6 +182,17 @@ void kernel(Params p) {
                     }
                 }
         }
+    };
+
+    const float sc = p.scale;
+    const float cu = BIAS != 0 ? kLog2e : sc * kLog2e;
+    float m_run = -INFINITY;  // running reference maximum, log2 units
+    float l_run = 0.f;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+
+    auto tile_step = [&](int j, int buf, const f32x4 (&bz)[NB][4]) __attribute__((always_inline)) {
         // S^T = K_tile Q^T.
         const uint16_t *Ks = Kbuf + buf * T::TILE;
         f32x16 s[NB];
@@ -269,17 +275,35 @@ void kernel(Params p) {
             }
     };
 
+    // The bias of tile j + 1 is read while tile j is computed (issued after
+    // tile j + 1's K/V copies, so the end-of-tile wait can leave it in flight):
+    // the bias is the kernel's only HBM stream without reuse, and a read issued
+    // at the top of its own tile would stall the tile for a full memory round
+    // trip.  Two register sets alternate, the loop unrolled by two.  The last
+    // tile also copies and reads "tile jhi + 1" (unused; reads past the K/V
+    // slice or the bias rows return zero): with no branch around the loads
+    // the compiler's count of outstanding loads stays exact, where a
+    // conditional prefetch makes it wait for the newest loads as well.
+    f32x4 bzA[NB][4], bzB[NB][4];
+    auto iter = [&](int j, const f32x4 (&cur)[NB][4], f32x4 (&nxt)[NB][4]) __attribute__((always_inline)) {
+        const int buf = (j - jlo) & 1;
+        load_kv(j + 1, buf ^ 1);
+        load_bias(j + 1, nxt);
+        if (active(j)) tile_step(j, buf, cur);
+        wait_vmcnt<BIAS_LOADS>();  // this wave's copies of tile j + 1 have landed
+        __syncthreads();
+    };
     if (jlo <= jhi) {
         load_kv(jlo, 0);
+        load_bias(jlo, bzA);
         wait_vmem();
         __syncthreads();
-        for (int j = jlo; j <= jhi; ++j) {
-            const int buf = (j - jlo) & 1;
-            if (j < jhi) load_kv(j + 1, buf ^ 1);
-            if (active(j)) tile_step(j, buf);
-            wait_vmem();
-            __syncthreads();
+        int j = jlo;
+        for (; j + 1 <= jhi; j += 2) {
+            iter(j, bzA, bzB);
+            iter(j + 1, bzB, bzA);
         }
+        if (j <= jhi) iter(j, bzA, bzB);
     }
 
     const float l_tot = pair_sum(l_run);
