@@ -23,9 +23,15 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // 1. Scores, bf16: S[bh, i, j] = sum_c Q[bh, i, c] K[bh, j, c]  (fp32 accumulate,
-//    rounded to bf16).  Workgroup tile: 128 queries x 128 keys, 4 waves x 32
-//    queries; same S^T = K Q^T MFMA orientation as the fused kernel.
+//    rounded to bf16).  A workgroup takes 128 queries (4 waves x 32) and
+//    SCORES_KPW consecutive 128-key blocks; same S^T = K Q^T MFMA orientation
+//    as the fused kernel.
 // ---------------------------------------------------------------------------
+// Key blocks per workgroup: Q stays in registers across them, and each
+// block's stores drain while the next block's K tile loads and multiplies
+// (dense 8k: 1 block 31.4-32.0 ms for the whole unfused path, 8 blocks
+// 29.5-29.8, 16 30.0, 64 32.4).
+constexpr int SCORES_KPW = 8;
 template <int D, bool VEC>
 __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t *__restrict__ Q,
                                                           const uint16_t *__restrict__ K,
@@ -36,9 +42,10 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t *__rest
     constexpr int LDS_ELEMS = (128 * KSTR > 128 * SSTR) ? 128 * KSTR : 128 * SSTR;
     __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
 
+    const int nkg = (nkb + SCORES_KPW - 1) / SCORES_KPW;  // key-block groups per query block
     const int logical = xcd_remap(blockIdx.x, gridDim.x, xcds);
-    const int kb = logical % nkb;
-    const int rest = logical / nkb;
+    const int kg = logical % nkg;
+    const int rest = logical / nkg;
     const int qb = rest % nqb;
     const int bh = rest / nqb;
 
@@ -49,55 +56,61 @@ __global__ __launch_bounds__(256) void scores_bf16_kernel(const uint16_t *__rest
     const auto rq = make_rsrc(Q + slice, slice_bytes);
     const auto rk = make_rsrc(K + slice, slice_bytes);
 
-    const int key0 = kb * 128;
-    for (int c = tid; c < 128 * D / 8; c += 256) {
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        *reinterpret_cast<u32x4 *>(smem + row * KSTR + col8 * 8) =
-            buf_load16(rk, (uint32_t)((key0 + row) * D + col8 * 8) * 2u);
-    }
     const int qrow = qb * 128 + wave * 32 + l32;
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
         qf[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hf) * 2u));
-    __syncthreads();
 
-    f32x16 acc[4];
+    for (int kk = 0; kk < SCORES_KPW; ++kk) {
+        const int kb = kg * SCORES_KPW + kk;
+        if (kb >= nkb) break;
+        const int key0 = kb * 128;
+        if (kk > 0) __syncthreads();  // the previous tile's staged rows have been read
+        for (int c = tid; c < 128 * D / 8; c += 256) {
+            const int row = c / (D / 8), col8 = c % (D / 8);
+            *reinterpret_cast<u32x4 *>(smem + row * KSTR + col8 * 8) =
+                buf_load16(rk, (uint32_t)((key0 + row) * D + col8 * 8) * 2u);
+        }
+        __syncthreads();
+
+        f32x16 acc[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
+        for (int b = 0; b < 4; ++b) acc[b] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+        for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + (32 * b + l32) * KSTR + 16 * s + 8 * hf);
+                acc[b] = mfma32(a, qf[s], acc[b]);
+            }
+        }
+        __syncthreads();  // K tile no longer needed; reuse LDS to stage the output rows
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(smem + (32 * b + l32) * KSTR + 16 * s + 8 * hf);
-            acc[b] = mfma32(a, qf[s], acc[b]);
-        }
-    }
-    __syncthreads();  // K tile no longer needed; reuse LDS to stage the output rows
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            u32x2 w;
-            w[0] = pack_bf16x2(acc[b][4 * g], acc[b][4 * g + 1]);
-            w[1] = pack_bf16x2(acc[b][4 * g + 2], acc[b][4 * g + 3]);
-            *reinterpret_cast<u32x2 *>(smem + (wave * 32 + l32) * SSTR + 32 * b + 8 * g + 4 * hf) = w;
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(acc[b][4 * g], acc[b][4 * g + 1]);
+                w[1] = pack_bf16x2(acc[b][4 * g + 2], acc[b][4 * g + 3]);
+                *reinterpret_cast<u32x2 *>(smem + (wave * 32 + l32) * SSTR + 32 * b + 8 * g + 4 * hf) = w;
+            }
         }
-    }
-    __syncthreads();
-    for (int c = tid; c < 128 * 16; c += 256) {
-        const int row = c >> 4, col = (c & 15) * 8;
-        const int i = qb * 128 + row, j = key0 + col;
-        if (i >= N || j >= N) continue;
-        uint16_t *dst = S + ((size_t)bh * N + i) * N + j;
-        const uint16_t *src = smem + row * SSTR + col;
-        if (VEC) {
-            // S streams through (34 GB at the dense 8k shape, far beyond L2 and
-            // MALL): non-temporal stores measured 6 % faster for this kernel.
-            // (The same on the softmax's in-place accesses was 8 % slower.)
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst));
-        } else {
-            for (int e = 0; e < 8 && j + e < N; ++e) dst[e] = src[e];
+        __syncthreads();
+        for (int c = tid; c < 128 * 16; c += 256) {
+            const int row = c >> 4, col = (c & 15) * 8;
+            const int i = qb * 128 + row, j = key0 + col;
+            if (i >= N || j >= N) continue;
+            uint16_t *dst = S + ((size_t)bh * N + i) * N + j;
+            const uint16_t *src = smem + row * SSTR + col;
+            if (VEC) {
+                // S streams through (34 GB at the dense 8k shape, far beyond L2 and
+                // MALL): non-temporal stores measured 6 % faster for this kernel.
+                // (The same on the softmax's in-place accesses was 8 % slower.)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src), reinterpret_cast<u32x4 *>(dst));
+            } else {
+                for (int e = 0; e < 8 && j + e < N; ++e) dst[e] = src[e];
+            }
         }
     }
 }
@@ -552,7 +565,7 @@ hipError_t launch_bf16(const FwdArgs &a, void *ws, hipStream_t s) {
     auto *o = static_cast<uint16_t *>(a.o);
     auto *S = static_cast<uint16_t *>(ws);
     const int xcds = device_shape().xcds;
-    const unsigned g1 = (unsigned)a.BH * (unsigned)nqb * (unsigned)nqb;
+    const unsigned g1 = (unsigned)a.BH * (unsigned)nqb * (unsigned)((nqb + SCORES_KPW - 1) / SCORES_KPW);
     if (vec)
         hipLaunchKernelGGL((scores_bf16_kernel<D, true>), dim3(g1), dim3(256), 0, s, q, k, S, N, nqb, nqb, xcds);
     else
