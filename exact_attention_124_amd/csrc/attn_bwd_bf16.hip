@@ -19,8 +19,9 @@
 //      dK/dV kernel loads them straight into its S and dP accumulators as the
 //      MFMAs' starting values, so S' = S - lse/scale and dP' = dP - D come out
 //      of the matrix cores and P = exp2(scale log2(e) S'), dS = P dP';
-//   2. dK/dV: a workgroup owns 128 keys (four waves of 32), keeps their K and
-//      V rows in VGPRs and streams 32-query tiles of Q, dO through LDS;
+//   2. dK/dV: a workgroup owns 128 keys (four waves of 32), keeps their K
+//      rows in VGPRs and their V rows in LDS, and streams 32-query tiles of
+//      Q, dO (with the tile's statistics) through LDS;
 //   3. dQ:   a workgroup owns 128 queries, keeps their Q and dO rows in VGPRs
 //      and streams 64-key tiles of K, V through LDS (the forward's shape).
 //
