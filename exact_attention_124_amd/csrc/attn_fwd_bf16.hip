@@ -521,14 +521,29 @@ void persistent_kernel(Params p) {
 
         auto softmax = [&](int j, f32x16 (&s)[NB], bf16x8 (&pb)[2 * NB], bool masked) __attribute__((always_inline)) {
             if (masked) {
+                // Per 32-key block (wave-uniform tests): keys all at or before
+                // the wave's first query and before N need no mask; keys all
+                // after its last query (or at or past N) are all removed; only
+                // the block on the wave's diagonal or across N compares each
+                // element.  Key of element r: k0 + 4*hf + cr, cr = 8*(r/4) + r%4,
+                // removed when cr > lim - k0 - 4*hf.
                 const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
+                    const int k0 = j * BC + 32 * b;
+                    const int last = CAUSAL ? min(q0, N - 1) : N - 1;  // last key every row of the wave sees
+                    const int first_out = CAUSAL ? min(q0 + 31, N - 1) : N - 1;  // keys past it are out for every row
+                    if (k0 + 31 <= last) continue;
+                    if (k0 > first_out) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = j * BC + 32 * b + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if (kk > lim) s[b][r] = -INFINITY;
+                        for (int r = 0; r < 16; ++r) s[b][r] = -INFINITY;
+                        continue;
                     }
+                    int rel = lim - k0 - 4 * hf;
+                    asm volatile("" : "+v"(rel));
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (8 * (r >> 2) + (r & 3) > rel) s[b][r] = -INFINITY;
                 }
             }
             float mx = s[0][0];
