@@ -46,6 +46,7 @@ PEAK_FP8_TFLOPS = 5033.2    # twice the bf16 rate (32x32x64 fp8 MFMA)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_attention_124_amd/csrc/attn_fwd_bf16.hip",
                   "exact_attention_124_amd/csrc/attn_fwd_bf16_dense.hip",
+                  "exact_attention_124_amd/csrc/attn_fwd_bf16_persistent.hip",
                   "exact_attention_124_amd/csrc/common.h",
                   "exact_attention_124_amd/build.py"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_fwd_bf16_dense_8k_traffic.json")

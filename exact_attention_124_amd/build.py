@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libattn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_dense.hip", "attn_fwd_f32.hip", "attn_unfused.hip",
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_dense.hip", "attn_fwd_bf16_persistent.hip",
+           "attn_fwd_f32.hip", "attn_unfused.hip",
            "attn_bwd_bf16.hip", "attn_fwd_fp8.hip", "attn_fwd_masked.hip", "ew_chain.hip"]
 # Per-file extra flags.  The fused bf16 kernel never produces or relies on NaN
 # (inputs are required to be finite), which lets max reductions use v_max3
@@ -29,7 +30,9 @@ SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_dense.hip", "attn
 EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"],
          "attn_fwd_fp8.hip": ["-fno-honor-nans"],
          # the non-causal 8-wave forward: LLVM's iterative ILP machine scheduler
-         "attn_fwd_bf16_dense.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+         "attn_fwd_bf16_dense.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+         # the persistent forward: LLVM's max-memory-clause machine scheduler
+         "attn_fwd_bf16_persistent.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 # The masked kernel compares against -inf and keeps rows at -inf on purpose,
 # so it is built with the default floating-point semantics.
 

@@ -997,15 +997,10 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
     const bool wide = blocks8 >= 192 && !(CAUSAL && a.N <= 1024);
     if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
-    if constexpr (CAUSAL) {
-        hipError_t e;
-        if (launch_persistent<D, true>(a, s, e)) return e;
-        return launch<D, CAUSAL, 8, 64, true>(a, s);
-    } else {
-        hipError_t e;
-        if (launch_persistent<D, false>(a, s, e)) return e;
-        return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
-    }
+    hipError_t e;
+    if (launch_fwd_bf16_persistent(a, s, e)) return e;  // instantiated in attn_fwd_bf16_persistent.hip
+    if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
+    else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s) {

@@ -27,6 +27,10 @@ struct FwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t s);
 // Non-causal 8-wave forward (attn_fwd_bf16_dense.hip); called by launch_fwd_bf16.
 hipError_t launch_fwd_bf16_dense8(const FwdArgs &a, hipStream_t s);
+// Persistent 8-wave forward (attn_fwd_bf16_persistent.hip); called by
+// launch_fwd_bf16.  Returns false (launching nothing) when B*H is not a
+// multiple of the device's XCD count; else sets err to the launch status.
+bool launch_fwd_bf16_persistent(const FwdArgs &a, hipStream_t s, hipError_t &err);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t s);
 
 // Fused forward on OCP e4m3 inputs with per-tensor dequantisation factors;
