@@ -110,55 +110,88 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
 
 # ---------------------------------------------------------------------------
 # Marshalling helpers (torch is only a container for device memory here).
+# They run on every call, so the accepted case costs a few attribute reads;
+# a failed check drops to a slow path that names what is wrong.
 # ---------------------------------------------------------------------------
+_T = None            # the torch module, imported on first use
+_get_device = None   # index of the current device
+_raw_stream = None   # raw handle of a device's current stream
+
+
 def _torch():
-    import torch
-    return torch
+    global _T, _get_device, _raw_stream
+    if _T is None:
+        import torch
+        _get_device = torch._C._cuda_getDevice
+        _raw_stream = torch._C._cuda_getCurrentRawStream
+        _T = torch
+    return _T
 
 
-def _check_qkv(q, k, v, dtype):
+def _qkv_error(names, tensors, dtype):
     torch = _torch()
-    if not isinstance(q, torch.Tensor):
-        raise TypeError("q must be a torch.Tensor")
-    shape = q.shape
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("q must live on a GPU")
-    if q.dtype != dtype:
-        raise TypeError(f"q must be {dtype}, got {q.dtype}")
-    if len(shape) != 4 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, H, N, d] tensor")
-    for name, t in (("k", k), ("v", v)):
+    pairs = list(zip(names, tensors))
+    for name, t in pairs:
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
+    for name, t in pairs:
         if t.dtype != dtype:
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if t.shape != shape:
-            raise ValueError("q, k and v must have the same shape")
-        if t.device != dev:
-            raise ValueError("q, k and v must be on the same device")
-        if not t.is_contiguous():
+    for name, t in pairs:
+        if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
-    return tuple(shape)
+    for name, t in pairs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must live on a GPU")
+    if any(t.shape != tensors[0].shape for t in tensors):
+        raise ValueError(f"{', '.join(names)} must have the same shape")
+    raise ValueError(f"{', '.join(names)} must be on the same device")
 
 
-def _check_out(o, lse, shape, dtype, device):
-    torch = _torch()
-    if o.dtype != dtype or o.shape != shape or o.device != device or not o.is_contiguous():
-        raise ValueError("o must be a contiguous tensor like q")
+def _check_qkv(q, k, v, dtype, names=("q", "k", "v")):
+    """(B, H, N, d, device index) of three contiguous, same-shape
+    [B, H, N, d] GPU tensors of ``dtype`` on one device; raises otherwise."""
+    try:
+        shape = q.shape
+        if (q.dtype is dtype and k.dtype is dtype and v.dtype is dtype and q.is_cuda
+                and len(shape) == 4 and k.shape == shape and v.shape == shape
+                and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+            dev = q.get_device()
+            if k.get_device() == dev and v.get_device() == dev:
+                B, H, N, d = shape
+                return B, H, N, d, dev
+    except AttributeError:
+        pass
+    _qkv_error(names, (q, k, v), dtype)
+
+
+def _check_out(o, lse, B, H, N, d, dtype, dev, name="o"):
+    """``o``: contiguous [B, H, N, d] of ``dtype`` on device ``dev``;
+    ``lse`` (if given): contiguous float32 [B, H, N] on the same device."""
+    try:
+        ok = (o.dtype is dtype and o.shape == (B, H, N, d) and o.is_contiguous()
+              and o.get_device() == dev)
+    except AttributeError:
+        ok = False
+    if not ok:
+        raise ValueError(f"{name} must be a contiguous {dtype} [B, H, N, d] tensor like q, on q's device")
     if lse is not None:
-        if lse.dtype != torch.float32 or lse.shape != shape[:3] or lse.device != device \
-                or not lse.is_contiguous():
+        try:
+            ok = (lse.dtype is _torch().float32 and lse.shape == (B, H, N) and lse.is_contiguous()
+                  and lse.get_device() == dev)
+        except AttributeError:
+            ok = False
+        if not ok:
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
 
 
-def _stream(stream, device):
+def _stream(stream, dev):
+    """Raw stream handle: the device's current stream when ``stream`` is
+    None, else an int handle or a torch stream's handle."""
     if stream is None:
-        torch = _torch()
-        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-        if raw is not None:  # the current stream's handle, without building a Stream object
-            return raw(device.index if device.index is not None else torch.cuda.current_device())
-        return torch.cuda.current_stream(device).cuda_stream
+        if _raw_stream is None:
+            _torch()
+        return _raw_stream(dev)
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -172,37 +205,48 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _launch(device, fn, *args):
-    """Call a C entry point with ``device`` current: its kernels are launched
-    on the current device, which must own the tensors and the stream.  The
-    device is switched (and restored) only when another one is current."""
-    torch = _torch()
-    if device.index is None or device.index == torch.cuda.current_device():
+def _launch(dev, fn, *args):
+    """Call a C entry point with device ``dev`` current: its kernels are
+    launched on the current device, which must own the tensors and the
+    stream.  The device is switched (and restored) only when another one is
+    current."""
+    if _get_device is None:
+        _torch()
+    if dev == _get_device():
         return fn(*args)
-    with torch.cuda.device(device):
+    with _T.cuda.device(dev):
         return fn(*args)
 
 
 def _fwd(name, dtype, q, k, v, o, lse, causal, scale, stream):
-    B, H, N, d = _check_qkv(q, k, v, dtype)
-    _check_out(o, lse, (B, H, N, d), dtype, q.device)
-    fn = getattr(load_library(), name)
-    st = _launch(q.device, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+    B, H, N, d, dev = _check_qkv(q, k, v, dtype)
+    _check_out(o, lse, B, H, N, d, dtype, dev)
+    st = _launch(dev, getattr(_lib or load_library(), name), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                 o.data_ptr(), None if lse is None else lse.data_ptr(), B, H, N, d,
+                 _scale(scale, d), 1 if causal else 0, _stream(stream, dev))
     if st != 0:
         raise AttnError(st, name)
 
 
-def _unfused(name, dtype, elem, q, k, v, o, lse, workspace, causal, scale, stream):
-    B, H, N, d = _check_qkv(q, k, v, dtype)
-    _check_out(o, lse, (B, H, N, d), dtype, q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
+def _workspace_bytes(workspace, dev):
+    """Size in bytes of a contiguous workspace tensor on device ``dev``."""
+    try:
+        ok = workspace.get_device() == dev and workspace.is_contiguous()
+    except AttributeError:
+        ok = False
+    if not ok:
         raise ValueError("workspace must be a contiguous tensor on q's device")
-    nbytes = workspace.numel() * workspace.element_size()
+    return workspace.numel() * workspace.element_size()
+
+
+def _unfused(name, dtype, elem, q, k, v, o, lse, workspace, causal, scale, stream):
+    B, H, N, d, dev = _check_qkv(q, k, v, dtype)
+    _check_out(o, lse, B, H, N, d, dtype, dev)
+    nbytes = _workspace_bytes(workspace, dev)
     fn = getattr(load_library(), name)
-    st = _launch(q.device, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
+    st = _launch(dev, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
                  workspace.data_ptr(), nbytes, B, H, N, d, _scale(scale, d), 1 if causal else 0,
-                 _stream(stream, q.device))
+                 _stream(stream, dev))
     if st != 0:
         raise AttnError(st, name)
 
@@ -235,23 +279,23 @@ def attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal=False, scale=None, s
 def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
     """fp8 (e4m3) fused forward into caller-allocated bf16 ``o`` (and ``lse``)."""
     torch = _torch()
-    B, H, N, d = _check_qkv(q, k, v, torch.float8_e4m3fn)
-    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
-    st = _launch(q.device, load_library().attn_fwd_fp8,
+    B, H, N, d, dev = _check_qkv(q, k, v, torch.float8_e4m3fn)
+    _check_out(o, lse, B, H, N, d, torch.bfloat16, dev)
+    st = _launch(dev, load_library().attn_fwd_fp8,
                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
                  B, H, N, d, _scale(scale, d), float(q_descale), float(k_descale),
-                 float(v_descale), 1 if causal else 0, _stream(stream, q.device))
+                 float(v_descale), 1 if causal else 0, _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd_fp8")
 
 
-def _bias_view(bias, B, H, N, device):
+def _bias_view(bias, B, H, N, dev):
     """(pointer, stride_b, stride_h, stride_i) of a float32 bias broadcastable
     to [B, H, N, N]: shape [N, N] or [B|1, H|1, N, N], last stride 1."""
     torch = _torch()
     if bias is None:
         return None, 0, 0, 0
-    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.device != device:
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.get_device() != dev:
         raise TypeError("bias must be a float32 tensor on q's device")
     if bias.dim() == 2:
         bias = bias.unsqueeze(0).unsqueeze(0)
@@ -268,14 +312,14 @@ def attn_fwd_masked(q, k, v, o, lse=None, causal=False, window=(-1, -1), bias=No
     float32 additive bias, into caller-allocated ``o`` (and ``lse``).
     ``window`` = (left, right); a negative side is unbounded."""
     torch = _torch()
-    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
-    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
-    bp, sb, sh, si = _bias_view(bias, B, H, N, q.device)
+    B, H, N, d, dev = _check_qkv(q, k, v, torch.bfloat16)
+    _check_out(o, lse, B, H, N, d, torch.bfloat16, dev)
+    bp, sb, sh, si = _bias_view(bias, B, H, N, dev)
     wl, wr = (int(window[0]), int(window[1]))
-    st = _launch(q.device, load_library().attn_fwd_masked,
+    st = _launch(dev, load_library().attn_fwd_masked,
                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
                  B, H, N, d, _scale(scale, d), 1 if causal else 0, wl, wr, bp, sb, sh, si,
-                 _stream(stream, q.device))
+                 _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd_masked")
 
@@ -286,14 +330,15 @@ def _ew(name, x, y, bias, scale, stream):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() \
                 or t.device.type != "cuda":
             raise ValueError(f"{nm} must be a contiguous bf16 [rows, cols] tensor on a GPU")
-    if tuple(y.shape) != tuple(x.shape) or y.device != x.device:
+    dev = x.get_device()
+    if y.shape != x.shape or y.get_device() != dev:
         raise ValueError("y must have x's shape and device")
     if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or tuple(bias.shape) != (x.shape[1],) \
-            or not bias.is_contiguous() or bias.device != x.device:
+            or not bias.is_contiguous() or bias.get_device() != dev:
         raise ValueError("bias must be a contiguous float32 [cols] tensor on x's device")
-    st = _launch(x.device, getattr(load_library(), name),
+    st = _launch(dev, getattr(load_library(), name),
                  x.data_ptr(), y.data_ptr(), bias.data_ptr(), x.shape[0], x.shape[1],
-                 float(scale), _stream(stream, x.device))
+                 float(scale), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, name)
 
@@ -315,25 +360,29 @@ def elementwise_chain(x, bias, scale, fused=True, stream=None):
     return y
 
 
-def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
-    """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv``."""
-    torch = _torch()
-    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
-    _check_qkv(o, dout, dout, torch.bfloat16)
-    if tuple(o.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d):
-        raise ValueError("o and dout must have q's shape")
-    for t in (dq, dk, dv):
-        _check_out(t, None, (B, H, N, d), torch.bfloat16, q.device)
-    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
+def _check_bwd(q, k, v, o, lse, dout, dq, dk, dv):
+    """(B, H, N, d, device index) for the backward's tensors: bf16 q, k, v,
+    o, dout, dq, dk, dv of one [B, H, N, d] shape and float32 lse [B, H, N],
+    all contiguous on one GPU."""
     if lse is None:
         raise ValueError("lse (the forward's log-sum-exp) is required")
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    st = _launch(q.device, load_library().attn_bwd,
+    bf16 = _torch().bfloat16
+    B, H, N, d, dev = _check_qkv(q, k, v, bf16)
+    _check_out(o, lse, B, H, N, d, bf16, dev)
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_out(t, None, B, H, N, d, bf16, dev, name)
+    return B, H, N, d, dev
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=False, scale=None, stream=None):
+    """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv``."""
+    B, H, N, d, dev = _check_bwd(q, k, v, o, lse, dout, dq, dk, dv)
+    nbytes = _workspace_bytes(workspace, dev)
+    st = _launch(dev, load_library().attn_bwd,
                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+                 workspace.data_ptr(), nbytes,
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_bwd")
 
@@ -342,20 +391,11 @@ def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None
     """bf16 backward into caller-allocated ``dq``, ``dk``, ``dv`` with the
     statistics in the library's static per-GPU scratch (no workspace, no
     allocation).  Calls that overlap on one GPU race on that scratch."""
-    torch = _torch()
-    B, H, N, d = _check_qkv(q, k, v, torch.bfloat16)
-    _check_qkv(o, dout, dout, torch.bfloat16)
-    if tuple(o.shape) != (B, H, N, d) or tuple(dout.shape) != (B, H, N, d):
-        raise ValueError("o and dout must have q's shape")
-    for t in (dq, dk, dv):
-        _check_out(t, None, (B, H, N, d), torch.bfloat16, q.device)
-    _check_out(o, lse, (B, H, N, d), torch.bfloat16, q.device)
-    if lse is None:
-        raise ValueError("lse (the forward's log-sum-exp) is required")
-    st = _launch(q.device, load_library().attn_bwd_noalloc,
+    B, H, N, d, dev = _check_bwd(q, k, v, o, lse, dout, dq, dk, dv)
+    st = _launch(dev, load_library().attn_bwd_noalloc,
                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, q.device))
+                 B, H, N, d, _scale(scale, d), 1 if causal else 0, _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_bwd_noalloc")
 

@@ -298,6 +298,30 @@ def test_python_binding_rejects_cpu_tensors(lib):
         ea.attention(x, x, x)
 
 
+def test_python_binding_names_what_is_wrong(lib):
+    # Every rejection happens before any GPU call, so CPU tensors exercise it.
+    import torch
+    import exact_attention_124_amd as ea
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    o = torch.empty_like(x)
+    with pytest.raises(TypeError, match="k must be a torch.Tensor"):
+        ea.attn_fwd(x, x.numpy, x, o)
+    with pytest.raises(TypeError, match="v must be torch.bfloat16"):
+        ea.attn_fwd(x, x, x.float(), o)
+    with pytest.raises(TypeError, match="q must be torch.float32"):
+        ea.attn_fwd_f32(x, x, x, o)
+    with pytest.raises(ValueError, match="k must be a contiguous"):
+        ea.attn_fwd(x, x.transpose(2, 3), x, o)
+    with pytest.raises(ValueError, match="q must be a contiguous"):
+        ea.attn_fwd(x[0], x[0], x[0], o)
+    with pytest.raises(ValueError, match="must live on a GPU"):
+        ea.attn_fwd(x, x, x, o)
+    with pytest.raises(TypeError, match="q must be torch.float8_e4m3fn"):
+        ea.attn_fwd_fp8(x, x, x, o, None, 1.0, 1.0, 1.0)
+    with pytest.raises(ValueError, match="lse .* is required"):
+        ea.attn_bwd_noalloc(x, x, x, o, None, x, o, o, o)
+
+
 def test_no_oracle_in_product_path():
     # The product package neither imports nor links the oracle.
     pkg = os.path.join(ROOT, "exact_attention_124_amd")
