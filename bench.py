@@ -621,27 +621,32 @@ def main():
                 continue
             ww = WORKLOADS[name]
             tot, pl = bench_fused(ea, ww, max(5, args.steps // 2), 3)
-            lm = sum(pl) / len(pl)
-            if lm < 0.05:  # launches of a few microseconds: average many more
+            pm = sum(pl) / len(pl)
+            if pm < 0.05:  # launches of a few microseconds: average many more
                 tot, pl = bench_fused(ea, ww, 200, 20)
-                lm = sum(pl) / len(pl)
+                pm = sum(pl) / len(pl)
+            # Per-call time of back-to-back binding calls between two events;
+            # a per-launch event pair adds its own GPU time, which matters for
+            # calls of a few microseconds.
+            calls = 200 if pm < 1.0 else max(5, args.steps // 2)
+            lm, host_us = bench_fused_back_to_back(ea, ww, calls)
             gm = bench_fused_graph(ea, ww) if lm < 1.0 else None
             sweep.append({"workload": name, "desc": ww.describe(), "launch_ms": round(lm, 4),
                           "TFLOP/s": round(ww.flops / (lm * 1e-3) / 1e12, 2),
-                          "frac_bf16_peak": round(ww.flops / (lm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+                          "frac_bf16_peak": round(ww.flops / (lm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "event_pair_launch_ms": round(pm, 4),
+                          "binding_host_us_per_call": round(host_us, 2)})
             if gm is not None:
-                bm, host_us = bench_fused_back_to_back(ea, ww)
                 sweep[-1].update({"graph_ms_per_call": round(gm, 4),
-                                  "graph_TFLOP/s": round(ww.flops / (gm * 1e-3) / 1e12, 2),
-                                  "back_to_back_ms_per_call": round(bm, 4),
-                                  "binding_host_us_per_call": round(host_us, 2)})
-                if lm < 0.05:
-                    sweep[-1]["raw_c_abi_launch_ms"] = round(bench_fused_raw(ea, ww, 200, 20), 4)
+                                  "graph_TFLOP/s": round(ww.flops / (gm * 1e-3) / 1e12, 2)})
+                if pm < 0.05:
+                    sweep[-1]["raw_c_abi_event_pair_launch_ms"] = round(bench_fused_raw(ea, ww, 200, 20), 4)
             if name in ("gpt2_heads_bf16", "causal_2k_bf16"):
                 cm = bench_fused_cold(ea, ww)
                 sweep[-1].update({"cold_launch_ms": round(cm, 4),
                                   "cold_note": "median of 10 calls, each after a 512 MiB buffer write"})
-            log(f"[bench] sweep {name}: {lm:.4f} ms per launch"
+            log(f"[bench] sweep {name}: {lm:.4f} ms per call back to back, {pm:.4f} ms per launch"
+                " between its own events"
                 + (f", {gm:.4f} ms per call in a graph" if gm is not None else "")
                 + f", {sweep[-1]['TFLOP/s']} TFLOP/s")
         sweep.insert(3, {"workload": HEADLINE, "desc": w.describe(), "launch_ms": round(launch_ms, 4),
