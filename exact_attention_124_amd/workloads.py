@@ -27,7 +27,8 @@ head dimensions the pages discuss, "d is 64 or 128", and a 12-head model):
 * 8-bit inputs: the float32 ``Q``, ``K``, ``V`` above, each divided by its
   per-tensor factor ``descale = max|x| / 448`` (float32) and converted to
   ``torch.float8_e4m3fn`` (round to nearest even; the largest magnitude lands
-  on 448, the largest finite E4M3 value).
+  on 448, the largest finite E4M3 value); for a tensor requested in E5M2,
+  ``descale = max|x| / 57344`` and ``torch.float8_e5m2``.
 """
 from __future__ import annotations
 
@@ -127,15 +128,22 @@ def make_chain(rows: int, cols: int, seed: int = 0, device="cpu"):
 E4M3_MAX = 448.0
 
 
-def make_qkv_fp8(B: int, H: int, N: int, d: int, seed: int = 0, q_mult: float = 1.0, device="cpu"):
+E5M2_MAX = 57344.0
+FP8_DTYPES = {"e4m3": (torch.float8_e4m3fn, E4M3_MAX), "e5m2": (torch.float8_e5m2, E5M2_MAX)}
+
+
+def make_qkv_fp8(B: int, H: int, N: int, d: int, seed: int = 0, q_mult: float = 1.0, device="cpu",
+                 formats=("e4m3", "e4m3", "e4m3")):
     """8-bit Q, K, V and their float32 dequantisation factors (see the module
-    docstring): returns ``(q8, k8, v8, q_descale, k_descale, v_descale)``."""
+    docstring), in the (q, k, v) ``formats`` ("e4m3" or "e5m2"): returns
+    ``(q8, k8, v8, q_descale, k_descale, v_descale)``."""
     qkv = make_qkv(B, H, N, d, torch.float32, seed, q_mult)
     out, scales = [], []
-    for t in qkv:
+    for t, fmt in zip(qkv, formats):
+        dtype, fmax = FP8_DTYPES[fmt]
         amax = float(t.abs().max()) if t.numel() else 1.0
-        ds = torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32)
-        t8 = (t / ds).to(torch.float8_e4m3fn)
+        ds = torch.tensor(amax / fmax if amax > 0 else 1.0, dtype=torch.float32)
+        t8 = (t / ds).to(dtype)
         out.append(t8.to(device) if str(device) != "cpu" else t8)
         scales.append(float(ds))
     return (*out, *scales)

@@ -10,7 +10,7 @@ textbook forward: scores, row max, exp-sum, weighted values),
 ``attn_bwd_oracle.c`` (its gradients), ``attn_probs_oracle.c`` (rows of the
 probability matrix) and ``attn_masked_oracle.c`` (forward with window masks
 and an additive bias).  This module builds them with gcc and marshals numpy
-arrays through ctypes; the e4m3 decoding and the elementwise chain
+arrays through ctypes; the e4m3 and e5m2 decoding and the elementwise chain
 (relu(scale * x + bias)) are written out here in numpy.
 
 Definition followed: grasp.study lesson on standard self-attention, section
@@ -191,19 +191,63 @@ def decode_e4m3(codes) -> np.ndarray:
     return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, val)
 
 
-def dequantize_fp8(t8, descale: float) -> np.ndarray:
-    """``descale * decode_e4m3(t8)`` in fp64 (exact)."""
-    return decode_e4m3(t8) * float(np.float32(descale))
+def decode_e5m2(codes) -> np.ndarray:
+    """Value of each OCP FP8 E5M2 byte as float64, written out from the format
+    definition: 1 sign bit, 5 exponent bits with bias 15, 2 mantissa bits;
+    exponent field 0 encodes subnormals m * 2^-16; the all-ones exponent
+    encodes infinity with a zero mantissa (0x7C, 0xFC) and NaN otherwise, so
+    the largest finite value is 1.75 * 2^15 = 57344.
+
+    ``codes``: uint8 array, or a torch float8_e5m2 / uint8 tensor (read as raw
+    bytes, never converted by torch)."""
+    if hasattr(codes, "detach"):
+        import torch
+        t = codes.detach().to("cpu").contiguous()
+        if t.dtype != torch.uint8:
+            t = t.view(torch.uint8)
+        codes = t.numpy()
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 2) & 0x1F
+    m = (b & 0x3).astype(np.float64)
+    normal = (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = (m / 4.0) * 2.0 ** -14
+    val = sign * np.where(e == 0, sub, normal)
+    special = np.where((b & 0x3) == 0, sign * np.inf, np.nan)
+    return np.where(e == 0x1F, special, val)
+
+
+FP8_FORMATS = ("e4m3", "e5m2")
+
+
+def fp8_format_of(t) -> str:
+    """``"e5m2"`` for a torch float8_e5m2 tensor, else ``"e4m3"``."""
+    return "e5m2" if str(getattr(t, "dtype", "")) == "torch.float8_e5m2" else "e4m3"
+
+
+def decode_fp8(codes, fmt: str) -> np.ndarray:
+    """:func:`decode_e4m3` or :func:`decode_e5m2` by ``fmt``."""
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    return decode_e4m3(codes) if fmt == "e4m3" else decode_e5m2(codes)
+
+
+def dequantize_fp8(t8, descale: float, fmt: str | None = None) -> np.ndarray:
+    """``descale * decode(t8)`` in fp64 (exact); the format is ``fmt``, else
+    that of ``t8``'s torch dtype."""
+    return decode_fp8(t8, fmt or fp8_format_of(t8)) * float(np.float32(descale))
 
 
 def attention_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float, scale: float,
-                  causal: bool = False, rows=None, threads: int = 0):
+                  causal: bool = False, rows=None, threads: int = 0, formats=None):
     """Exact attention of dequantised 8-bit inputs: the inputs are
-    ``descale * decode_e4m3(code)`` per tensor (exact in fp64: a 4-bit
-    significand times an fp32 factor), then :func:`attention` in fp64."""
-    qd, kd, vd = (float(np.float32(x)) for x in (q_descale, k_descale, v_descale))
-    return attention(decode_e4m3(q8) * qd, decode_e4m3(k8) * kd, decode_e4m3(v8) * vd, scale, causal,
-                     rows=rows, threads=threads)
+    ``descale * decode(code)`` per tensor (exact in fp64: a 4- or 3-bit
+    significand times an fp32 factor), then :func:`attention` in fp64.
+    ``formats``: (q, k, v) formats, each ``"e4m3"`` or ``"e5m2"``; by default
+    each tensor's torch dtype decides (anything but float8_e5m2 is E4M3)."""
+    fq, fk, fv = formats if formats is not None else (fp8_format_of(q8), fp8_format_of(k8), fp8_format_of(v8))
+    return attention(dequantize_fp8(q8, q_descale, fq), dequantize_fp8(k8, k_descale, fk),
+                     dequantize_fp8(v8, v_descale, fv), scale, causal, rows=rows, threads=threads)
 
 
 def attention_masked(q, k, v, scale: float, causal: bool = False, window_left: int = -1,
