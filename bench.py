@@ -19,7 +19,8 @@ Prints ONE JSON line.  Besides the headline value it carries:
   backward      -- attn_bwd (dQ, dK, dV) on the dense 8k and causal 32k
                    workloads;
   fp8           -- attn_fwd_fp8 (e4m3 Q, K, V, bf16 O) on the dense 8k and
-                   causal 32k shapes, against the fp8 dense MFMA peak;
+                   causal 32k shapes, and with e5m2 inputs on dense 8k,
+                   against the fp8 dense MFMA peak;
   masked        -- attn_fwd_masked: dense 8k with an [N, N] fp32 bias, and
                    causal 32k with a 4096-key sliding window (FLOPs counted
                    over allowed (query, key) pairs only);
@@ -274,11 +275,13 @@ def bench_backward(ea, w, steps, warmup):
     return total_ms, per
 
 
-def bench_fp8(ea, w, steps, warmup):
-    """Time attn_fwd_fp8 on the shape of workload `w` (inputs quantised to e4m3)."""
+def bench_fp8(ea, w, steps, warmup, fmt="e4m3"):
+    """Time attn_fwd_fp8 on the shape of workload `w` (inputs quantised to
+    `fmt`, e4m3 or e5m2, all three tensors)."""
     import torch
     from exact_attention_124_amd.workloads import make_qkv_fp8
-    q8, k8, v8, qd, kd, vd = make_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.q_mult, device="cuda")
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.q_mult, device="cuda",
+                                          formats=(fmt,) * 3)
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -307,15 +310,16 @@ def backward_legs(ea, workloads, steps, warmup):
 
 def fp8_legs(ea, workloads, steps, warmup):
     out = []
-    for name in (HEADLINE, "causal_32k_qx8_bf16"):
+    for name, fmt in ((HEADLINE, "e4m3"), ("causal_32k_qx8_bf16", "e4m3"), (HEADLINE, "e5m2")):
         ww = workloads[name]
-        tot, pl = bench_fp8(ea, ww, steps, warmup)
+        tot, pl = bench_fp8(ea, ww, steps, warmup, fmt)
         fm = sum(pl) / len(pl)
         tf = ww.flops / (fm * 1e-3) / 1e12
-        out.append({"workload": name.replace("_bf16", "_fp8"), "shape": ww.describe().replace("bf16", "e4m3"),
+        tag = "_fp8" if fmt == "e4m3" else "_fp8_e5m2"
+        out.append({"workload": name.replace("_bf16", tag), "shape": ww.describe().replace("bf16", fmt),
                     "ms": round(fm, 4), "TFLOP/s": round(tf, 2),
                     "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
-        log(f"[bench] fp8 {name}: {fm:.4f} ms, {out[-1]['TFLOP/s']} TFLOP/s")
+        log(f"[bench] fp8 {fmt} {name}: {fm:.4f} ms, {out[-1]['TFLOP/s']} TFLOP/s")
     return out
 
 

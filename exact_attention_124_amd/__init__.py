@@ -20,7 +20,7 @@ __all__ = [
     "attn_last_hip_error", "attention", "attention_unfused", "STATUS", "attn_bwd",
     "attn_bwd_workspace_bytes", "attention_backward", "attn_fwd_fp8", "attention_fp8",
     "attn_fwd_masked", "attention_masked", "ew_chain_fused", "ew_chain_unfused", "elementwise_chain",
-    "attn_bwd_noalloc", "BWD_SCRATCH_BYTES",
+    "attn_bwd_noalloc", "BWD_SCRATCH_BYTES", "attn_fwd_fp8_fmt", "FP8_FORMATS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,8 @@ STATUS = {
 }
 # ATTN_BWD_SCRATCH_BYTES (include/attn.h): attn_bwd_noalloc's static statistics buffer per GPU
 BWD_SCRATCH_BYTES = 16 << 20
+# ATTN_FP8_E4M3 / ATTN_FP8_E5M2 (include/attn.h): input formats of attn_fwd_fp8_fmt
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
 class AttnError(RuntimeError):
@@ -76,6 +78,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, P]
     lib.attn_fwd_fp8.restype = I
+    lib.attn_fwd_fp8_fmt.argtypes = [P, P, P, P, P, I, I, I, I, F, F, F, F, I, I, I, I, P]
+    lib.attn_fwd_fp8_fmt.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, SZ, I, I, I, I, F, I, P]
     lib.attn_bwd.restype = I
     lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
@@ -276,17 +280,57 @@ def attn_fwd_unfused_f32(q, k, v, o, lse, workspace, causal=False, scale=None, s
              scale, stream)
 
 
-def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
-    """fp8 (e4m3) fused forward into caller-allocated bf16 ``o`` (and ``lse``)."""
+def _fp8_formats(q, k, v):
+    """ATTN_FP8_* code of each of q, k, v from its torch dtype
+    (float8_e4m3fn: E4M3, float8_e5m2: E5M2); raises for any other."""
     torch = _torch()
-    B, H, N, d, dev = _check_qkv(q, k, v, torch.float8_e4m3fn)
+    codes = {torch.float8_e4m3fn: FP8_FORMATS["e4m3"], torch.float8_e5m2: FP8_FORMATS["e5m2"]}
+    out = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in codes:
+            raise TypeError(f"{name} must be torch.float8_e4m3fn or torch.float8_e5m2, got {t.dtype}")
+        out.append(codes[t.dtype])
+    return out
+
+
+def _fwd_fp8(name, q, k, v, o, lse, q_descale, k_descale, v_descale, formats, causal, scale, stream):
+    torch = _torch()
+    u8 = torch.uint8
+    B, H, N, d, dev = _check_qkv(q.view(u8), k.view(u8), v.view(u8), u8)
     _check_out(o, lse, B, H, N, d, torch.bfloat16, dev)
-    st = _launch(dev, load_library().attn_fwd_fp8,
-                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse),
-                 B, H, N, d, _scale(scale, d), float(q_descale), float(k_descale),
-                 float(v_descale), 1 if causal else 0, _stream(stream, dev))
+    lib = load_library()
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse), B, H, N, d, _scale(scale, d),
+            float(q_descale), float(k_descale), float(v_descale)]
+    if name == "attn_fwd_fp8_fmt":
+        args += [int(f) for f in formats]
+    st = _launch(dev, getattr(lib, name), *args, 1 if causal else 0, _stream(stream, dev))
     if st != 0:
-        raise AttnError(st, "attn_fwd_fp8")
+        raise AttnError(st, name)
+
+
+def attn_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
+    """fp8 fused forward into caller-allocated bf16 ``o`` (and ``lse``).  Each
+    of q, k, v is a torch float8_e4m3fn (OCP E4M3) or float8_e5m2 (OCP E5M2)
+    tensor; all E4M3 calls the C ``attn_fwd_fp8``, any E5M2 input
+    ``attn_fwd_fp8_fmt`` with the three formats."""
+    formats = _fp8_formats(q, k, v)
+    name = "attn_fwd_fp8" if not any(formats) else "attn_fwd_fp8_fmt"
+    _fwd_fp8(name, q, k, v, o, lse, q_descale, k_descale, v_descale, formats, causal, scale, stream)
+
+
+def attn_fwd_fp8_fmt(q, k, v, o, lse, q_descale, k_descale, v_descale, q_format, k_format, v_format,
+                     causal=False, scale=None, stream=None):
+    """The C ``attn_fwd_fp8_fmt``: q, k, v are 1-byte tensors (uint8 or
+    either float8 dtype) whose bytes are read in the given formats
+    (``FP8_FORMATS["e4m3"]`` or ``FP8_FORMATS["e5m2"]``)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.element_size() != 1:
+            raise TypeError(f"{name} must be a tensor of 1-byte elements")
+    _fwd_fp8("attn_fwd_fp8_fmt", q, k, v, o, lse, q_descale, k_descale, v_descale,
+             (q_format, k_format, v_format), causal, scale, stream)
 
 
 def _bias_view(bias, B, H, N, dev):
@@ -418,7 +462,8 @@ def attention(q, k, v, causal=False, scale=None, stream=None):
 
 
 def attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
-    """fp8 fused forward; returns ``(o, lse)`` with ``o`` in bf16."""
+    """fp8 fused forward (each input E4M3 or E5M2 by its torch dtype); returns
+    ``(o, lse)`` with ``o`` in bf16."""
     torch = _torch()
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)

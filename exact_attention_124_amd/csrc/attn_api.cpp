@@ -214,17 +214,29 @@ int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float
     return finish(attn::launch_fwd_f32(make_args(q, k, v, o, lse, B, H, N, d, scale, causal), stream));
 }
 
-int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
-                 float scale, float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream) {
+int attn_fwd_fp8_fmt(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+                     int d, float scale, float q_descale, float k_descale, float v_descale, int q_format,
+                     int k_format, int v_format, int causal, hipStream_t stream) {
     const int st = validate_fp8(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal);
     if (st < 0) return ATTN_OK;
     if (st != ATTN_OK) return st;
+    for (int f : {q_format, k_format, v_format})
+        if (f != ATTN_FP8_E4M3 && f != ATTN_FP8_E5M2) return ATTN_ERR_ARG;
     attn::Fp8Args a;
     a.f = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
     a.q_descale = q_descale;
     a.k_descale = k_descale;
     a.v_descale = v_descale;
+    a.q_format = q_format;
+    a.k_format = k_format;
+    a.v_format = v_format;
     return finish(attn::launch_fwd_fp8(a, stream));
+}
+
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
+                 float scale, float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream) {
+    return attn_fwd_fp8_fmt(q, k, v, o, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, ATTN_FP8_E4M3,
+                            ATTN_FP8_E4M3, ATTN_FP8_E4M3, causal, stream);
 }
 
 int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N, int d,
@@ -343,7 +355,9 @@ const char *attn_status_string(int status) {
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_bytes() reports";
         case ATTN_ERR_HIP: return "HIP runtime error (see attn_last_hip_error)";
-        case ATTN_ERR_ARG: return "scale and fp8 descale factors must be finite and > 0, causal must be 0 or 1";
+        case ATTN_ERR_ARG:
+            return "scale and fp8 descale factors must be finite and > 0, causal must be 0 or 1, fp8 formats "
+                   "ATTN_FP8_E4M3 or ATTN_FP8_E5M2";
         case ATTN_ERR_SCRATCH:
             return "attn_bwd_noalloc: B*H*round_up(N,32) rows of statistics exceed its static scratch "
                    "(ATTN_BWD_SCRATCH_BYTES); use attn_bwd with a workspace";

@@ -1,5 +1,5 @@
-// Fused exact attention forward with fp8 (OCP e4m3) Q, K, V, bf16 output,
-// fp32 accumulation, gfx950.
+// Fused exact attention forward with 8-bit floating-point Q, K, V (OCP e4m3
+// or e5m2, chosen per tensor), bf16 output, fp32 accumulation, gfx950.
 //
 // The function is the one of the bf16 kernel ("The Attention Bottleneck --
 // and How FlashAttention Fixed It", section "The fix: tiling and fusion, never
@@ -25,6 +25,9 @@
 //    of one head dim to every lane.  The key order of the four reads matches
 //    the order in which the score accumulator holds its keys.
 //  * O = v_descale * acc / l, stored as bf16; lse as in the bf16 kernel.
+// The input formats are template arguments (the matrix instruction takes each
+// operand's format as an immediate); both formats are bytes, so loads,
+// layouts and transposes are the same for either.
 // Tiles are 128 keys, double-buffered in LDS (32 KiB per K or V tile pair at
 // d = 128); causal skipping, the pairing of long and short causal query blocks
 // and the XCD remap follow the bf16 kernel.
@@ -39,14 +42,19 @@ namespace fwd_fp8 {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// v_mfma_f32_32x32x64_f8f6f4 with both operands e4m3 and no block scales:
-// C(32x32) += A(32x64) * B(64x32).  Lane l supplies row (l % 32) of A and
-// column (l % 32) of B as 32 bytes; A and B use the same assignment of
+// Operand format codes of v_mfma_*_f8f6f4: 0 = fp8 (OCP e4m3), 1 = bf8 (OCP
+// e5m2).  The probabilities (B operand of the second product) are always e4m3.
+enum Fp8Format { kE4M3 = 0, kE5M2 = 1 };
+
+// v_mfma_f32_32x32x64_f8f6f4, A in format FA, B in format FB, no block
+// scales: C(32x32) += A(32x64) * B(64x32).  Lane l supplies row (l % 32) of A
+// and column (l % 32) of B as 32 bytes; A and B use the same assignment of
 // (lane half, byte) to the contraction index, so any consistent packing of
 // both operands contracts correctly.  The result layout is that of the bf16
 // 32x32 MFMA.
+template <int FA, int FB>
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t *p) {
@@ -135,7 +143,7 @@ struct Layout {
 
 constexpr float kLazyThreshold = 8.0f;  // log2 units; probabilities stay <= 2^8 < 448
 
-template <int D, bool CAUSAL, int WAVES, int BC>
+template <int D, bool CAUSAL, int WAVES, int BC, int FQ, int FK, int FV>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kernel(Params p) {
     using T = Tile<D, WAVES, BC>;
@@ -226,7 +234,7 @@ void kernel(Params p) {
                 for (int b = 0; b < NB; ++b) {
                     const u32x4 w[2] = {lds_read16(Ks + L::k_read(st, b, 0, lane)),
                                         lds_read16(Ks + L::k_read(st, b, 1, lane))};
-                    s[b] = mfma_f8(__builtin_bit_cast(i32x8, w), qf[st], s[b]);
+                    s[b] = mfma_f8<FK, FQ>(__builtin_bit_cast(i32x8, w), qf[st], s[b]);
                 }
             }
         };
@@ -303,7 +311,7 @@ void kernel(Params p) {
                                         lds_read_tr8(Vg + L::v_read(1, t, lane)),
                                         lds_read_tr8(Vg + L::v_read(2, t, lane)),
                                         lds_read_tr8(Vg + L::v_read(3, t, lane))};
-                    acc[t] = mfma_f8(__builtin_bit_cast(i32x8, w), pf[g], acc[t]);
+                    acc[t] = mfma_f8<FV, kE4M3>(__builtin_bit_cast(i32x8, w), pf[g], acc[t]);
                 }
             }
         };
@@ -360,7 +368,7 @@ void kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL, int WAVES, int BC>
+template <int D, bool CAUSAL, int WAVES, int BC, int FQ, int FK, int FV>
 hipError_t launch(const Fp8Args &a, hipStream_t s) {
     using T = Tile<D, WAVES, BC>;
     Params p;
@@ -376,7 +384,7 @@ hipError_t launch(const Fp8Args &a, hipStream_t s) {
     p.paired = CAUSAL && pair_causal_blocks((long long)a.f.BH * p.nqb, WAVES == 8 ? 1 : 2);
     p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.f.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
-    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC>), dim3(blocks), dim3(T::THREADS), 0, s, p);
+    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, FQ, FK, FV>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -387,17 +395,33 @@ hipError_t launch(const Fp8Args &a, hipStream_t s) {
 // at least four such workgroups per CU, else 4 waves (128 rows, two
 // workgroups per CU); causal sequences always take 4 waves, whose shorter
 // blocks waste less work on the diagonal.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FQ, int FK, int FV>
 static hipError_t launch_fp8_d(const Fp8Args &a, hipStream_t s) {
     using namespace fwd_fp8;
     const long long blocks8 = (long long)a.f.BH * ((a.f.N + 255) / 256);
     const bool wide = !CAUSAL && blocks8 >= 4 * 256;
-    return wide ? launch<D, CAUSAL, 8, 128>(a, s) : launch<D, CAUSAL, 4, 128>(a, s);
+    return wide ? launch<D, CAUSAL, 8, 128, FQ, FK, FV>(a, s) : launch<D, CAUSAL, 4, 128, FQ, FK, FV>(a, s);
 }
 
+template <int FQ, int FK, int FV>
+static hipError_t launch_fp8_f(const Fp8Args &a, hipStream_t s) {
+    if (a.f.d == 128)
+        return a.f.causal ? launch_fp8_d<128, true, FQ, FK, FV>(a, s) : launch_fp8_d<128, false, FQ, FK, FV>(a, s);
+    return a.f.causal ? launch_fp8_d<64, true, FQ, FK, FV>(a, s) : launch_fp8_d<64, false, FQ, FK, FV>(a, s);
+}
+
+// Formats: 0 = e4m3, 1 = e5m2 (validated by the caller).
 hipError_t launch_fwd_fp8(const Fp8Args &a, hipStream_t s) {
-    if (a.f.d == 128) return a.f.causal ? launch_fp8_d<128, true>(a, s) : launch_fp8_d<128, false>(a, s);
-    return a.f.causal ? launch_fp8_d<64, true>(a, s) : launch_fp8_d<64, false>(a, s);
+    switch (a.q_format * 4 + a.k_format * 2 + a.v_format) {
+    case 0: return launch_fp8_f<0, 0, 0>(a, s);
+    case 1: return launch_fp8_f<0, 0, 1>(a, s);
+    case 2: return launch_fp8_f<0, 1, 0>(a, s);
+    case 3: return launch_fp8_f<0, 1, 1>(a, s);
+    case 4: return launch_fp8_f<1, 0, 0>(a, s);
+    case 5: return launch_fp8_f<1, 0, 1>(a, s);
+    case 6: return launch_fp8_f<1, 1, 0>(a, s);
+    default: return launch_fp8_f<1, 1, 1>(a, s);
+    }
 }
 #endif
 

@@ -40,6 +40,9 @@ struct Fp8Args {
     float q_descale;
     float k_descale;
     float v_descale;
+    int q_format;  // 0 = OCP e4m3, 1 = OCP e5m2
+    int k_format;
+    int v_format;
 };
 hipError_t launch_fwd_fp8(const Fp8Args &a, hipStream_t s);
 

@@ -55,7 +55,7 @@ typedef enum {
     ATTN_ERR_ALIAS = 5,     /* an output range overlaps an input or another output range   */
     ATTN_ERR_WORKSPACE = 6, /* workspace smaller than attn_unfused_workspace_bytes / attn_bwd_workspace_bytes */
     ATTN_ERR_HIP = 7,       /* a HIP runtime call failed (see attn_last_hip_error)        */
-    ATTN_ERR_ARG = 8,       /* scale (or an fp8 descale) not finite and > 0, or causal not 0/1 */
+    ATTN_ERR_ARG = 8,       /* scale (or an fp8 descale) not finite and > 0, causal not 0/1, or an unknown fp8 format */
     ATTN_ERR_SCRATCH = 9    /* attn_bwd_noalloc: the statistics exceed the library's static scratch */
 } attn_status;
 
@@ -107,6 +107,26 @@ int attn_fwd_f32(const float *q, const float *k, const float *v, float *o, float
 int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int H, int N, int d, float scale,
                  float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream);
+
+/* 8-bit formats of attn_fwd_fp8_fmt's inputs. */
+enum { ATTN_FP8_E4M3 = 0, ATTN_FP8_E5M2 = 1 };
+
+/*
+ * attn_fwd_fp8 with the 8-bit format of each input chosen separately:
+ * q_format, k_format, v_format each ATTN_FP8_E4M3 (as attn_fwd_fp8) or
+ * ATTN_FP8_E5M2, the OCP FP8 E5M2 format (1 sign bit, 5 exponent bits with
+ * bias 15, 2 mantissa bits; subnormals; 0x7C and 0xFC are infinities and
+ * 0x7D-0x7F, 0xFD-0xFF NaN, which the caller must not pass; largest finite
+ * value 57344).  The function computed is the same (the inputs dequantised
+ * from their formats); the probabilities are still rounded to E4M3 before
+ * the second product.  Checks: as attn_fwd_fp8; a format other than the two
+ * returns ATTN_ERR_ARG.  attn_fwd_fp8 is this call with all three formats
+ * ATTN_FP8_E4M3.
+ */
+int attn_fwd_fp8_fmt(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int H, int N, int d, float scale,
+                     float q_descale, float k_descale, float v_descale,
+                     int q_format, int k_format, int v_format, int causal, hipStream_t stream);
 
 /*
  * Fused forward with a general mask and an additive bias, bfloat16: the

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_unfused", "attn_fwd_unfused_f32",
                             "attn_unfused_workspace_bytes", "attn_status_string",
                             "attn_last_hip_error", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_fwd_masked",
-                            "attn_bwd_noalloc"])
+                            "attn_bwd_noalloc", "attn_fwd_fp8_fmt"])
 
 
 def test_ew_header_declares_the_chain():
@@ -168,6 +168,27 @@ def test_fp8_validation_codes(lib):
     assert fp8(lib, o=V - 65536 + 16) == S["ATTN_ERR_ALIAS"]   # o's tail runs into v
     assert fp8(lib, lse=O + 65536 - 4) == S["ATTN_ERR_ALIAS"]  # lse starts inside o
     assert fp8(lib, N=1 << 26, d=128) == S["ATTN_ERR_SHAPE"]   # 32-bit slice offsets of o
+
+
+def fp8_fmt(lib, fq=0, fk=0, fv=0, q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=256, d=64, scale=0.125, qd=0.01,
+            kd=0.02, vd=0.03, causal=0):
+    return lib.attn_fwd_fp8_fmt(q, k, v, o, lse, B, H, N, d, scale, qd, kd, vd, fq, fk, fv, causal, None)
+
+
+def test_fp8_format_validation_codes(lib):
+    S = __import__("exact_attention_124_amd").STATUS
+    # Every call below fails validation or is empty: nothing is launched.
+    for f in (-1, 2, 3, 255):
+        assert fp8_fmt(lib, fq=f) == S["ATTN_ERR_ARG"]
+        assert fp8_fmt(lib, fk=f) == S["ATTN_ERR_ARG"]
+        assert fp8_fmt(lib, fv=f) == S["ATTN_ERR_ARG"]
+    assert fp8_fmt(lib, N=0, fq=7) == S["ATTN_OK"]  # empty: a no-op, as every entry point
+    assert fp8_fmt(lib, 1, 1, 1, q=None) == S["ATTN_ERR_NULL"]
+    assert fp8_fmt(lib, 1, 0, 1, d=96) == S["ATTN_ERR_HEAD_DIM"]
+    assert fp8_fmt(lib, 1, 1, 0, qd=0.0) == S["ATTN_ERR_ARG"]
+    assert fp8_fmt(lib, 0, 1, 1, o=Q + 16) == S["ATTN_ERR_ALIAS"]
+    assert fp8_fmt(lib, 1, 1, 1, k=K + 8) == S["ATTN_ERR_ALIGN"]
+    assert "fp8 formats" in lib.attn_status_string(S["ATTN_ERR_ARG"]).decode()
 
 
 BIAS = A + 10 * GAP

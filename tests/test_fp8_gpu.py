@@ -1,5 +1,6 @@
-"""GPU parity of the fp8 (OCP E4M3) fused forward against the fp64 oracle on
-the dequantised inputs.
+"""GPU parity of the fp8 fused forward (OCP E4M3 inputs, and E5M2 or mixed
+formats through attn_fwd_fp8_fmt) against the fp64 oracle on the
+dequantised inputs.
 
 Tolerance, derived from the kernel's arithmetic.  Both sides see the same
 inputs exactly (an E4M3 code times an fp32 factor), and the scores, softmax
@@ -99,9 +100,9 @@ def test_gpt2_heads_full(ea, W, oracle_mod):
     check(oracle_mod, o, lse, q8, k8, v8, qd, kd, vd, 1 / 8, False, "gpt2 heads")
 
 
-def _sliced(ea, W, oracle_mod, B, H, N, d, causal, q_mult, n_slices, n_rows, label):
-    say(f"[fp8] {label} B={B} H={H} N={N} d={d} causal={causal} q_mult={q_mult} (sampled)")
-    q8, k8, v8, qd, kd, vd = W.make_qkv_fp8(B, H, N, d, seed=0, q_mult=q_mult)
+def _sliced(ea, W, oracle_mod, B, H, N, d, causal, q_mult, n_slices, n_rows, label, formats=("e4m3",) * 3):
+    say(f"[fp8] {label} B={B} H={H} N={N} d={d} causal={causal} q_mult={q_mult} formats={formats} (sampled)")
+    q8, k8, v8, qd, kd, vd = W.make_qkv_fp8(B, H, N, d, seed=0, q_mult=q_mult, formats=formats)
     o, lse = run(ea, q8, k8, v8, qd, kd, vd, causal)
     g = torch.Generator().manual_seed(1)
     slices = torch.randperm(B * H, generator=g)[:n_slices].tolist()
@@ -152,3 +153,64 @@ def test_rejects_bad_descale_and_dtype(ea, W):
             ea.attention_fp8(q8, k8, v8, qd, bad, vd)
     with pytest.raises(TypeError):
         ea.attention_fp8(q8.view(torch.uint8), k8, v8, qd, kd, vd)
+
+
+# ---------------------------------------------------------------------------
+# Inputs in OCP E5M2, alone or mixed with E4M3 (attn_fwd_fp8_fmt).  Both
+# sides read the same codes exactly and the kernel still rounds P to E4M3, so
+# the bound above holds unchanged.
+# ---------------------------------------------------------------------------
+ALL_FORMATS = [(a, b, c) for a in ("e4m3", "e5m2") for b in ("e4m3", "e5m2") for c in ("e4m3", "e5m2")]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("formats", ALL_FORMATS)
+def test_formats_small(ea, W, oracle_mod, formats, d, causal):
+    N = 257
+    q8, k8, v8, qd, kd, vd = W.make_qkv_fp8(1, 2, N, d, seed=11 + d, q_mult=2.0, formats=formats)
+    say(f"[fp8] formats={formats} B=1 H=2 N={N} d={d} causal={causal}")
+    o, lse = run(ea, q8, k8, v8, qd, kd, vd, causal)
+    check(oracle_mod, o, lse, q8, k8, v8, qd, kd, vd, 1 / math.sqrt(d), causal, f"{formats} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [1, 17, 1000])
+def test_e5m2_ragged(ea, W, oracle_mod, N):
+    f = ("e5m2",) * 3
+    q8, k8, v8, qd, kd, vd = W.make_qkv_fp8(2, 3, N, 64, seed=N, q_mult=4.0, formats=f)
+    say(f"[fp8] e5m2 B=2 H=3 N={N} d=64 causal")
+    o, lse = run(ea, q8, k8, v8, qd, kd, vd, True)
+    check(oracle_mod, o, lse, q8, k8, v8, qd, kd, vd, 1 / 8, True, f"e5m2 N={N}")
+
+
+def test_dense_8k_e5m2(ea, W, oracle_mod):
+    _sliced(ea, W, oracle_mod, 8, 32, 8192, 128, False, 1.0, 2, 64, "dense 8k e5m2", formats=("e5m2",) * 3)
+
+
+def test_causal_2k_e5m2_values(ea, W, oracle_mod):
+    _sliced(ea, W, oracle_mod, 4, 32, 2048, 128, True, 1.0, 2, 2048, "causal 2k, e5m2 V",
+            formats=("e4m3", "e4m3", "e5m2"))
+
+
+def test_fmt_entry_reads_bytes_in_the_given_formats(ea, W, oracle_mod):
+    f = ("e5m2", "e4m3", "e5m2")
+    q8, k8, v8, qd, kd, vd = (t.cuda() if torch.is_tensor(t) else t
+                              for t in W.make_qkv_fp8(1, 4, 300, 128, seed=12, formats=f))
+    say("[fp8] attn_fwd_fp8_fmt on raw bytes, B=1 H=4 N=300 d=128")
+    o1, l1 = ea.attention_fp8(q8, k8, v8, qd, kd, vd, causal=True)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    F = ea.FP8_FORMATS
+    u8 = [t.view(torch.uint8) for t in (q8, k8, v8)]
+    ea.attn_fwd_fp8_fmt(*u8, o2, l2, qd, kd, vd, F["e5m2"], F["e4m3"], F["e5m2"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # The same bytes read as all-E4M3 are another input, and the kernel
+    # follows that reading: it matches the oracle for it.
+    o3, l3 = torch.empty_like(o1), torch.empty_like(l1)
+    ea.attn_fwd_fp8_fmt(*u8, o3, l3, qd, kd, vd, 0, 0, 0, causal=True)
+    torch.cuda.synchronize()
+    assert not torch.equal(o3, o1)
+    cpu = [t.cpu() for t in u8]  # uint8: the oracle reads these as E4M3
+    check(oracle_mod, o3.cpu(), l3.cpu(), *cpu, qd, kd, vd, 1 / math.sqrt(128), True, "bytes read as e4m3")
+    with pytest.raises(ea.AttnError):
+        ea.attn_fwd_fp8_fmt(*u8, o3, l3, qd, kd, vd, 2, 0, 0)
