@@ -23,7 +23,7 @@
 //    staging), double-buffered so tile j+1 lands while tile j is computed.
 //    K feeds the first product with ds_read_b128; the V^T operand of the
 //    second product comes from ds_read_b64_tr_b16 (LDS transpose read).
-//  * KAHEAD: K runs one tile ahead of V, so the score MFMAs of tile j+1 are
+//  * K runs one tile ahead of V, so the score MFMAs of tile j+1 are
 //    issued before the softmax of tile j and execute on the matrix unit while
 //    the vector unit exponentiates.
 //  * Lazy rescaling: the running maximum is only moved (and the accumulator
@@ -111,7 +111,7 @@ struct Layout {
 
 constexpr float kLazyThreshold = 8.0f;  // log2 units
 
-template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
+template <int D, bool CAUSAL, int WAVES, int BC>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void kernel(Params p) {
     using T = Tile<D, WAVES, BC>;
@@ -291,70 +291,47 @@ void kernel(Params p) {
             }
         };
 
-        if constexpr (KAHEAD) {
-            // During iteration j the LDS holds K(j+1) and V(j); K(j+2) and V(j+1)
-            // are in flight, into the buffers K(j) and V(j-1) have vacated.
-            load_k(0, 0);
-            load_v(0, 0);
-            if (ntiles > 1) load_k(1, 1);
+        // During iteration j the LDS holds K(j+1) and V(j); K(j+2) and V(j+1)
+        // are in flight, into the buffers K(j) and V(j-1) have vacated.
+        load_k(0, 0);
+        load_v(0, 0);
+        if (ntiles > 1) load_k(1, 1);
+        wait_vmem();
+        __syncthreads();
+        f32x16 sa[NB], sb[NB];
+        if (active(0)) scores(0, sa);
+        // The first step refills K buffer 0 (tile 2); every wave must have
+        // finished reading tile 0 from it first.
+        __syncthreads();
+        // CHECKED is false for steps whose tiles j and j+1 are both below
+        // nfull: every wave visits them and no key needs a mask, so the
+        // main loop carries no per-tile tests; the remaining steps (the
+        // diagonal of a causal block, a ragged last tile) run checked.
+        auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB], auto checked) __attribute__((always_inline)) {
+            constexpr bool CHECKED = decltype(checked)::value;
+            if (j + 2 < ntiles) load_k(j + 2, j & 1);
+            if (!CHECKED || j + 1 < ntiles) {
+                load_v(j + 1, (j + 1) & 1);
+                if (!CHECKED || active(j + 1)) scores((j + 1) & 1, nxt);
+            }
+            if (!CHECKED || active(j)) {
+                bf16x8 pb[2 * NB];
+                softmax(j, cur, pb, CHECKED && j >= nfull);
+                pv(j & 1, pb);
+            }
             wait_vmem();
             __syncthreads();
-            f32x16 sa[NB], sb[NB];
-            if (active(0)) scores(0, sa);
-            // The first step refills K buffer 0 (tile 2); every wave must have
-            // finished reading tile 0 from it first.
-            __syncthreads();
-            // CHECKED is false for steps whose tiles j and j+1 are both below
-            // nfull: every wave visits them and no key needs a mask, so the
-            // main loop carries no per-tile tests; the remaining steps (the
-            // diagonal of a causal block, a ragged last tile) run checked.
-            auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB], auto checked) __attribute__((always_inline)) {
-                constexpr bool CHECKED = decltype(checked)::value;
-                if (j + 2 < ntiles) load_k(j + 2, j & 1);
-                if (!CHECKED || j + 1 < ntiles) {
-                    load_v(j + 1, (j + 1) & 1);
-                    if (!CHECKED || active(j + 1)) scores((j + 1) & 1, nxt);
-                }
-                if (!CHECKED || active(j)) {
-                    bf16x8 pb[2 * NB];
-                    softmax(j, cur, pb, CHECKED && j >= nfull);
-                    pv(j & 1, pb);
-                }
-                wait_vmem();
-                __syncthreads();
-            };
-            int j = 0;
-            for (; j + 2 < nfull; j += 2) {
-                step(j, sa, sb, std::false_type{});
-                step(j + 1, sb, sa, std::false_type{});
-            }
-            for (; j + 1 < ntiles; j += 2) {
-                step(j, sa, sb, std::true_type{});
-                step(j + 1, sb, sa, std::true_type{});
-            }
-            if (j < ntiles) step(j, sa, sb, std::true_type{});
-        } else {
-            load_k(0, 0);
-            load_v(0, 0);
-            wait_vmem();
-            __syncthreads();
-            for (int j = 0; j < ntiles; ++j) {
-                const int buf = j & 1;
-                if (j + 1 < ntiles) {
-                    load_k(j + 1, buf ^ 1);
-                    load_v(j + 1, buf ^ 1);
-                }
-                if (active(j)) {
-                    f32x16 s[NB];
-                    bf16x8 pb[2 * NB];
-                    scores(buf, s);
-                    softmax(j, s, pb, j >= nfull);
-                    pv(buf, pb);
-                }
-                wait_vmem();
-                __syncthreads();
-            }
+        };
+        int j = 0;
+        for (; j + 2 < nfull; j += 2) {
+            step(j, sa, sb, std::false_type{});
+            step(j + 1, sb, sa, std::false_type{});
         }
+        for (; j + 1 < ntiles; j += 2) {
+            step(j, sa, sb, std::true_type{});
+            step(j + 1, sb, sa, std::true_type{});
+        }
+        if (j < ntiles) step(j, sa, sb, std::true_type{});
 
         // Epilogue: O = acc / l, lse = ln(2) * (m + log2 l).
         const float l_tot = pair_sum(l_run);
@@ -956,7 +933,7 @@ bool launch_persistent(const FwdArgs &a, hipStream_t s, hipError_t &err) {
     return true;
 }
 
-template <int D, bool CAUSAL, int WAVES, int BC, bool KAHEAD>
+template <int D, bool CAUSAL, int WAVES, int BC>
 hipError_t launch(const FwdArgs &a, hipStream_t s) {
     using T = Tile<D, WAVES, BC>;
     Params p;
@@ -971,7 +948,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
     p.paired = CAUSAL && pair_causal_blocks((long long)a.BH * p.nqb, WAVES == 8 ? 1 : 2);
     p.xcds = device_shape().xcds;
     const unsigned blocks = (unsigned)a.BH * (unsigned)(p.paired ? (p.nqb + 1) / 2 : p.nqb);
-    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC, KAHEAD>), dim3(blocks), dim3(T::THREADS), 0, s, p);
+    hipLaunchKernelGGL((kernel<D, CAUSAL, WAVES, BC>), dim3(blocks), dim3(T::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -979,13 +956,20 @@ hipError_t launch(const FwdArgs &a, hipStream_t s) {
 
 #ifndef ATTN_FWD_BF16_NO_DEFAULT_LAUNCHER
 // 8 waves (256 query rows) per workgroup share each K/V tile and run the
-// K-ahead pipeline.  4 waves (128 rows, two workgroups per CU, plain loop)
+// K-ahead pipeline.  4 waves (128 rows, two workgroups per CU, also K-ahead:
+// 2-14 % faster than the plain loop on these shapes, bit for bit the same)
 // are used when there would be fewer than 192 8-wave workgroups (three
 // quarters of one per CU: at 128 the 8-wave grid leaves half the CUs idle and
-// measured 11-13 % slower, at 192 and above it measured up to 15 % faster),
-// and for causal sequences up to 1024 keys, where the waves of a 256-row block
-// differ by up to 3.5 tiles of causal work and the shorter block wastes more
-// of the whole.  When
+// measured 11-13 % slower, at 192 and above it measured up to 15 % faster);
+// for causal sequences up to 1280 keys (2048 at d = 64), where the waves of a
+// 256-row block differ by up to 3.5 tiles of causal work and the shorter
+// block wastes more of the whole (4 waves measured 10-11 % faster at 1280
+// keys, 3 % slower at 1536 with d = 128; 3-7 % faster at 1536 and 2048 with
+// d = 64); and for dense grids of one to four rounds of 8-wave workgroups
+// that end in a partial round, whose last round the 8-wave grid runs with
+// CUs idle while two 4-wave workgroups per CU spread it (measured 2-20 %
+// faster at 1.25, 1.5, 2.5 and 3.5 rounds; 2-6 % slower at whole rounds and
+// 5-6 % slower below one round).  When
 // even the 4-wave grid has at most 128 workgroups (half a workgroup per CU),
 // the split-key kernel runs instead: four times the workgroups, each wave a
 // quarter of the keys (measured 8-37 % faster there, 40 % slower at 256).
@@ -995,11 +979,14 @@ static hipError_t launch_d(const FwdArgs &a, hipStream_t s) {
     const long long blocks4 = (long long)a.BH * ((a.N + 127) / 128);
     if (blocks4 <= 128) return launch_split<D, CAUSAL>(a, s);
     const long long blocks8 = (long long)a.BH * ((a.N + 255) / 256);
-    const bool wide = blocks8 >= 192 && !(CAUSAL && a.N <= 1024);
-    if (!wide) return launch<D, CAUSAL, 4, 64, false>(a, s);
+    const long long cus = device_shape().cus;
+    bool wide = blocks8 >= 192;
+    if (CAUSAL) wide = wide && a.N > (D == 64 ? 2048 : 1280);
+    else if (blocks8 > cus && blocks8 < 4 * cus && blocks8 % cus != 0) wide = false;
+    if (!wide) return launch<D, CAUSAL, 4, 64>(a, s);
     hipError_t e;
     if (launch_fwd_bf16_persistent(a, s, e)) return e;  // instantiated in attn_fwd_bf16_persistent.hip
-    if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64, true>(a, s);
+    if constexpr (CAUSAL) return launch<D, CAUSAL, 8, 64>(a, s);
     else return launch_fwd_bf16_dense8(a, s);  // instantiated in attn_fwd_bf16_dense.hip
 }
 

@@ -422,7 +422,7 @@ def test_rejects_bad_head_dim_on_device(ea):
 def test_schedule_independence(ea, W):
     # The same slice computed inside a large batch (eight-wave workgroups,
     # K-ahead pipeline) and in a batch of copies of it small enough for
-    # four-wave workgroups (plain loop) visits the same key tiles in the same
+    # four-wave workgroups visits the same key tiles in the same
     # order for every row, with the same 32-row wave, so the results must agree
     # bit for bit.  Alone, the slice takes the split-key kernel, which sums the
     # keys in another order: it must agree within the bf16 tolerance.
@@ -471,3 +471,30 @@ def test_persistent_matches_per_block_kernel(ea, W, oracle_mod, causal, N):
                                   rows=rows)
     rw = torch.tensor(rows, device=o_all.device)
     check_bf16(o_all[0, 60:][:, rw], l_all[0, 60:][:, rw], ro, rl, "persistent, last slices")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 20, 4096, 128, False),   # 1.25 rounds of 8-wave workgroups: 4-wave grid
+    (1, 24, 2048, 64, False),    # 0.75 rounds: 8-wave (persistent) grid
+    (1, 36, 4000, 128, False),   # 2.25 rounds, ragged: 4-wave grid
+    (8, 16, 1280, 128, True),    # causal, 1280 keys: 4-wave grid
+    (4, 16, 2000, 64, True),     # causal d = 64 up to 2048 keys: 4-wave grid
+    (2, 32, 1300, 128, True),    # causal past 1280 keys at d = 128: 8-wave grid
+])
+def test_launch_shapes_match_oracle(ea, W, oracle_mod, B, H, N, d, causal):
+    # The grids the launcher chooses between four- and eight-wave workgroups
+    # (both with K one tile ahead), each checked on every row of two slices;
+    # the same slice in a grid of copies large enough for eight-wave
+    # workgroups must agree bit for bit (same tiles, same order per row).
+    q, k, v = (t.cuda() for t in W.make_qkv(B, H, N, d, torch.bfloat16, seed=1500 + N + d))
+    say(f"[launch shape] B={B} H={H} N={N} d={d} causal={causal}")
+    o, lse = ea.attention(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    for idx in (0, B * H - 1):
+        b, h = divmod(idx, H)
+        ro, rl = oracle_mod.attention(q[b, h].cpu(), k[b, h].cpu(), v[b, h].cpu(), 1 / math.sqrt(d), causal)
+        check_bf16(o[b, h], lse[b, h], ro, rl, f"slice {idx}")
+    qs, ks, vs = (t[:1, :1].expand(1, 64, N, d).contiguous() for t in (q, k, v))
+    o64, l64 = ea.attention(qs, ks, vs, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o64[0, 63], o[0, 0]) and torch.equal(l64[0, 63], lse[0, 0])
