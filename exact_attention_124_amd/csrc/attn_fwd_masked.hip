@@ -192,10 +192,9 @@ void kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
 
-    auto tile_step = [&](int j, int buf, const f32x4 (&bz)[NB][4]) __attribute__((always_inline)) {
-        // S^T = K_tile Q^T.
+    // S^T = K_tile Q^T.
+    auto scores = [&](int buf, f32x16 (&s)[NB]) __attribute__((always_inline)) {
         const uint16_t *Ks = Kbuf + buf * T::TILE;
-        f32x16 s[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
@@ -203,6 +202,10 @@ void kernel(Params p) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 s[b] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + L::k_read(st, b, lane)), qf[st], s[b]);
+    };
+    // Bias, mask and online softmax of score tile j, then O^T += V^T P^T with
+    // V from LDS buffer buf.
+    auto softmax_pv = [&](int j, int buf, f32x16 (&s)[NB], const f32x4 (&bz)[NB][4]) __attribute__((always_inline)) {
         // Natural-log scores with bias and mask.
         const bool masked = !full(j);
         int lo = 0, hi = N - 1;
@@ -274,6 +277,11 @@ void kernel(Params p) {
                 acc[t] = mfma32(__builtin_bit_cast(bf16x8, w), pb[st], acc[t]);
             }
     };
+    auto tile_step = [&](int j, int buf, const f32x4 (&bz)[NB][4]) __attribute__((always_inline)) {
+        f32x16 s[NB];
+        scores(buf, s);
+        softmax_pv(j, buf, s, bz);
+    };
 
     // The bias of tile j + 1 is read while tile j is computed (issued after
     // tile j + 1's K/V copies, so the end-of-tile wait can leave it in flight):
@@ -285,6 +293,52 @@ void kernel(Params p) {
     // the compiler's count of outstanding loads stays exact, where a
     // conditional prefetch makes it wait for the newest loads as well.
     f32x4 bzA[NB][4], bzB[NB][4];
+    if constexpr (BIAS == 0) {
+        // Without a bias, K runs one tile ahead of V as in the bf16 kernel:
+        // during step j the LDS holds K(j+1) and V(j), and K(j+2) and V(j+1)
+        // are in flight, so the score products of tile j+1 are issued before
+        // the softmax of tile j.  (With a bias the second score buffer does
+        // not fit beside the bias registers.)
+        auto load_k = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(tile * BC * D) * 2u);
+#pragma unroll
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                load16_lds_async_so(rk, k_off[n], base, Kbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+        };
+        auto load_v = [&](int tile, int buf) __attribute__((always_inline)) {
+            const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(tile * BC * D) * 2u);
+#pragma unroll
+            for (int n = 0; n < T::LOADS_PER_WAVE; ++n)
+                load16_lds_async_so(rv, v_off[n], base, Vbuf + buf * T::TILE + (wave + WAVES * n) * 512);
+        };
+        if (jlo <= jhi) {
+            load_k(jlo, 0);
+            load_v(jlo, 0);
+            if (jlo + 1 <= jhi) load_k(jlo + 1, 1);
+            wait_vmem();
+            __syncthreads();
+            f32x16 sa[NB], sb[NB];
+            if (active(jlo)) scores(0, sa);
+            __syncthreads();  // K buffer 0 is refilled (tile jlo + 2) in the first step
+            auto step = [&](int j, f32x16 (&cur)[NB], f32x16 (&nxt)[NB]) __attribute__((always_inline)) {
+                const int buf = (j - jlo) & 1;
+                if (j + 2 <= jhi) load_k(j + 2, buf);
+                if (j + 1 <= jhi) {
+                    load_v(j + 1, buf ^ 1);
+                    if (active(j + 1)) scores(buf ^ 1, nxt);
+                }
+                if (active(j)) softmax_pv(j, buf, cur, bzA);
+                wait_vmem();
+                __syncthreads();
+            };
+            int j = jlo;
+            for (; j + 1 <= jhi; j += 2) {
+                step(j, sa, sb);
+                step(j + 1, sb, sa);
+            }
+            if (j <= jhi) step(j, sa, sb);
+        }
+    }
     auto iter = [&](int j, const f32x4 (&cur)[NB][4], f32x4 (&nxt)[NB][4]) __attribute__((always_inline)) {
         const int buf = (j - jlo) & 1;
         load_kv(j + 1, buf ^ 1);
@@ -293,7 +347,7 @@ void kernel(Params p) {
         wait_vmcnt<BIAS_LOADS>();  // this wave's copies of tile j + 1 have landed
         __syncthreads();
     };
-    if (jlo <= jhi) {
+    if (BIAS != 0 && jlo <= jhi) {
         load_kv(jlo, 0);
         load_bias(jlo, bzA);
         wait_vmem();
